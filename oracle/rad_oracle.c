@@ -1,0 +1,266 @@
+/*
+ * rad_oracle.c -- CPU oracle of the rotated W8A8 int8 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
+ * statement of what the GPU library computes.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the GPU library, and it includes nothing from
+ * it.  Plain C11 loops, OpenMP over independent rows only.  Built with -O2,
+ * -ffp-contract=off and without fast-math, so every float operation below is
+ * one IEEE-754 operation in the stated order.
+ *
+ * Source of what is computed: the model card "Qwen3.8-27B IQ8R + DFlash2 --
+ * radiance container".
+ *   - Table row "Weights": each trunk linear holds int8 codes in -127..127
+ *     with one u8 scale for every (row, 256 of K) and one bf16 scale per row
+ *     above it; every 128 of K is rotated by the Hadamard transform without
+ *     normalisation.  The lm_head holds int8 codes with one bf16 scale for
+ *     every (row, 128 of K).
+ *   - Table row "Activations": activations are int8 in the same rotated
+ *     domain (W8A8).
+ *   - Section "How this file was made": the trunk recipe rules name int8
+ *     codes, group 256, u8 scales under a per-row bf16 second scale, the
+ *     fwht128 transform and symmetric clamping; the output.weight rule names
+ *     int8 codes with group 128 and bf16 scales.
+ *
+ * Where the card is silent, the readings used here (each one is listed with
+ * its reason in the design notes of the repository):
+ *   R1  H is the 128x128 Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j);
+ *       the rotation of a block is v -> v.H with no 1/sqrt(128).
+ *   R2  Blocks are the contiguous runs [128c, 128c+128) of K.
+ *   R3  The f32 rotation is the radix-2 butterfly network with stage widths
+ *       h = 1, 2, 4, ..., 64 in that order; in each butterfly the sum goes to
+ *       the lower index and the difference (lower minus upper) to the upper.
+ *   R4  Activations are quantised per token over all of K: amax = max |x~|,
+ *       s = amax / 127 (f32 division), q = clamp(rne(x~ / s), -127, 127)
+ *       (f32 division, ties to even).  amax = 0 gives s = 0 and q = 0.
+ *   R5  A group partial P[m][n][g] is the exact integer sum over the K indices
+ *       of group g of q_x[m][k] * q_w[n][k]; it always fits int32.
+ *   R6  The u8 group scale is an integer multiplier: y = s_m * r_n * 2^-7 *
+ *       sum_g u8[n][g] * P[m][n][g]; the head: y = s_m * 2^-7 * sum_g
+ *       b[n][g] * P[m][n][g].  2^-7 undoes H.H^T = 128 I.  Evaluated in f64
+ *       and rounded once to f32.
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <math.h>
+#include <fenv.h>
+#include <omp.h>
+
+#define ORC_OK           0
+#define ORC_E_ARG       -1   /* a size, pointer or format is invalid      */
+#define ORC_E_OVERFLOW  -2   /* a group partial did not fit int32          */
+#define ORC_E_NONFINITE -3   /* an input activation was NaN or infinite    */
+#define ORC_E_ROUNDING  -4   /* the FPU is not in round-to-nearest-even    */
+
+#define ORC_FMT_U8G256_BF16ROW 0
+#define ORC_FMT_BF16G128       1
+
+int orc_num_threads(void) { return omp_get_max_threads(); }
+
+/* bf16 bits -> value.  A bf16 is the top half of an f32. */
+static double bf16_value(uint16_t bits)
+{
+    union { uint32_t u; float f; } c;
+    c.u = (uint32_t)bits << 16;
+    return (double)c.f;
+}
+
+/* One 128-point block, in place, in the butterfly order of reading R3. */
+static void fwht128_block(float *v)
+{
+    for (int h = 1; h < 128; h *= 2) {
+        for (int i = 0; i < 128; i += 2 * h) {
+            for (int j = i; j < i + h; ++j) {
+                float a = v[j];
+                float b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+}
+
+/* y = x rotated per 128-block, rows x K, row-major.  x == y is allowed. */
+int orc_fwht128(const float *x, float *y, int64_t rows, int64_t K)
+{
+    if (!x || !y || rows < 0 || K <= 0 || K % 128 != 0) return ORC_E_ARG;
+    int64_t nblocks = rows * (K / 128);
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblocks; ++b) {
+        float v[128];
+        for (int i = 0; i < 128; ++i) v[i] = x[b * 128 + i];
+        fwht128_block(v);
+        for (int i = 0; i < 128; ++i) y[b * 128 + i] = v[i];
+    }
+    return ORC_OK;
+}
+
+/*
+ * Per-token int8 quantisation (reading R4) of x, optionally rotating each
+ * 128-block first (rotate != 0).  q: int8 [M][K], s: f32 [M].
+ */
+int orc_quant_act_i8(const float *x, int8_t *q, float *s, int64_t M, int64_t K, int rotate)
+{
+    if (!x || !q || !s || M < 0 || K <= 0 || K % 128 != 0) return ORC_E_ARG;
+    if (fegetround() != FE_TONEAREST) return ORC_E_ROUNDING;
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const float *xm = x + m * K;
+        int8_t *qm = q + m * K;
+        float amax = 0.0f;
+        int bad = 0;
+        /* pass 1: rotate block by block and take the largest magnitude */
+        for (int64_t c = 0; c < K; c += 128) {
+            float v[128];
+            for (int i = 0; i < 128; ++i) v[i] = xm[c + i];
+            if (rotate) fwht128_block(v);
+            for (int i = 0; i < 128; ++i) {
+                if (!isfinite(v[i])) bad = 1;
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+        }
+        if (bad) {
+            #pragma omp critical
+            status = ORC_E_NONFINITE;
+            continue;
+        }
+        float sm = amax / 127.0f;
+        s[m] = sm;
+        /* pass 2: the same rotation again, then divide and round */
+        for (int64_t c = 0; c < K; c += 128) {
+            float v[128];
+            for (int i = 0; i < 128; ++i) v[i] = xm[c + i];
+            if (rotate) fwht128_block(v);
+            for (int i = 0; i < 128; ++i) {
+                int code = 0;
+                if (sm != 0.0f) {
+                    float t = v[i] / sm;
+                    float r = rintf(t);          /* ties to even in FE_TONEAREST */
+                    if (r > 127.0f) r = 127.0f;
+                    if (r < -127.0f) r = -127.0f;
+                    code = (int)r;
+                }
+                qm[c + i] = (int8_t)code;
+            }
+        }
+    }
+    return status;
+}
+
+/* Exact partials of one (token, weight row) pair over all groups (R5). */
+static int pair_partials(const int8_t *qx, const int8_t *qw, int64_t K, int64_t gw, int32_t *Prow)
+{
+    int64_t G = K / gw;
+    for (int64_t g = 0; g < G; ++g) {
+        int64_t acc = 0;
+        for (int64_t k = g * gw; k < (g + 1) * gw; ++k)
+            acc += (int64_t)qx[k] * (int64_t)qw[k];
+        if (acc > INT32_MAX || acc < INT32_MIN) return ORC_E_OVERFLOW;
+        Prow[g] = (int32_t)acc;
+    }
+    return ORC_OK;
+}
+
+static int64_t group_width(int fmt)
+{
+    if (fmt == ORC_FMT_U8G256_BF16ROW) return 256;
+    if (fmt == ORC_FMT_BF16G128) return 128;
+    return 0;
+}
+
+/* Epilogue of reading R6 for one output element. */
+static float pair_output(int fmt, const int32_t *Prow, int64_t G, float s_m,
+                         const void *gscale_row, const uint16_t *rscale_n)
+{
+    if (fmt == ORC_FMT_U8G256_BF16ROW) {
+        const uint8_t *u8 = (const uint8_t *)gscale_row;
+        int64_t S = 0;                                  /* exact */
+        for (int64_t g = 0; g < G; ++g) S += (int64_t)u8[g] * (int64_t)Prow[g];
+        double v = (double)s_m * bf16_value(*rscale_n) * 0x1p-7 * (double)S;
+        return (float)v;
+    } else {
+        const uint16_t *b = (const uint16_t *)gscale_row;
+        double acc = 0.0;
+        for (int64_t g = 0; g < G; ++g) acc += bf16_value(b[g]) * (double)Prow[g];
+        double v = (double)s_m * 0x1p-7 * acc;
+        return (float)v;
+    }
+}
+
+/*
+ * All group partials.  qx: int8 [M][K], qw: int8 [N][K], P: int32 [M][N][K/gw].
+ */
+int orc_group_partials(const int8_t *qx, const int8_t *qw, int32_t *P,
+                       int64_t M, int64_t N, int64_t K, int fmt)
+{
+    int64_t gw = group_width(fmt);
+    if (!qx || !qw || !P || gw == 0 || M < 0 || N < 0 || K <= 0 || K % gw != 0) return ORC_E_ARG;
+    int64_t G = K / gw;
+    int status = ORC_OK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, P + (m * N + n) * G);
+            if (rc != ORC_OK) {
+                #pragma omp critical
+                status = rc;
+            }
+        }
+    return status;
+}
+
+/*
+ * Epilogue from stored partials.  gscale: u8 [N][G] or bf16 bits [N][G];
+ * rscale: bf16 bits [N] for the u8 format, ignored for the head format.
+ */
+int orc_epilogue(const int32_t *P, const float *s, int fmt, const void *gscale,
+                 const uint16_t *rscale, float *y, int64_t M, int64_t N, int64_t G)
+{
+    if (!P || !s || !gscale || !y || group_width(fmt) == 0 || M < 0 || N < 0 || G <= 0)
+        return ORC_E_ARG;
+    if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
+    size_t esz = (fmt == ORC_FMT_U8G256_BF16ROW) ? 1 : 2;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = pair_output(fmt, P + (m * N + n) * G, G, s[m],
+                                       (const char *)gscale + (size_t)(n * G) * esz,
+                                       fmt == ORC_FMT_U8G256_BF16ROW ? rscale + n : NULL);
+    return ORC_OK;
+}
+
+/*
+ * The whole contraction plus epilogue without storing P: y f32 [M][N].
+ * Identical arithmetic to orc_group_partials followed by orc_epilogue.
+ */
+int orc_linear(const int8_t *qx, const float *s, const int8_t *qw, int fmt,
+               const void *gscale, const uint16_t *rscale, float *y,
+               int64_t M, int64_t N, int64_t K)
+{
+    int64_t gw = group_width(fmt);
+    if (!qx || !s || !qw || !gscale || !y || gw == 0 || M < 0 || N < 0 || K <= 0 || K % gw != 0)
+        return ORC_E_ARG;
+    if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
+    int64_t G = K / gw;
+    if (G > 4096) return ORC_E_ARG;
+    size_t esz = (fmt == ORC_FMT_U8G256_BF16ROW) ? 1 : 2;
+    int status = ORC_OK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int32_t Prow[4096];
+            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, Prow);
+            if (rc != ORC_OK) {
+                #pragma omp critical
+                status = rc;
+                continue;
+            }
+            y[m * N + n] = pair_output(fmt, Prow, G, s[m],
+                                       (const char *)gscale + (size_t)(n * G) * esz,
+                                       fmt == ORC_FMT_U8G256_BF16ROW ? rscale + n : NULL);
+        }
+    return status;
+}

@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated W8A8 int8 linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
+
+A step is one pass of the whole layer over one batch of synthetic input that
+is already resident in HBM: rotate + quantise the f32 activations
+(rad_quant_act_i8), then the int8 contraction and epilogue (rad_w8a8_gemv for
+M <= 128, rad_w8a8_gemm above).  The default workload is the single-token
+decode of the fused gate_up projection (M=1, K=5120, N=34816).
+
+The weights rotate over enough distinct copies (>= 1 GiB) that the 256 MiB
+last-level cache cannot serve a repeated read.  Steps are replayed from a HIP
+graph (one graph launch per round of copies) unless --eager is given.
+
+One JSON line is printed.  `value` is the step's algorithmic bytes (f32
+activations in, weight codes and scales in, f32 outputs out, each counted
+once) per second for M <= 128, or 2*M*N*K int8 operations per second for
+larger M.  `roofline` is the dominant kernel timed alone with HIP events on
+its own stream, against MI355X's published peak.  `cpu_baseline` is the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "W8A8 rotated linear: HBM GB/s (M≤128) and int8 TOPS (M=8192), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
+COPY_TARGET_BYTES = 1 << 30    # distinct weight bytes rotated through per round
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_gate_up")
+    ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def sizes(wl):
+    from rotated_w8a8_int8_amd import workloads as W
+    M, K, N, G = wl.M, wl.K, wl.N, wl.G
+    esz = 1 if wl.fmt == W.FMT_U8G256_BF16ROW else 2
+    wbytes = N * K + N * G * esz + (N * 2 if wl.fmt == W.FMT_U8G256_BF16ROW else 0)
+    return dict(
+        weight=wbytes,
+        step=M * K * 4 + wbytes + M * N * 4,                 # x, weights, y
+        contraction=wbytes + M * K + M * 4 + M * N * 4,      # q_x, s_x, weights, y
+        quant=M * K * 4 + M * K + M * 4,                     # x in, q_x and s_x out
+        ops=2 * M * N * K,
+    )
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rotated_w8a8_int8_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()                                            # fail loudly if not built
+
+    wl = W.WORKLOADS[args.workload]
+    sz = sizes(wl)
+    big = wl.M > B.RAD_GEMV_MAX_M
+    steps = args.steps if args.steps is not None else (20 if big else 3000)
+    warmup = args.warmup if args.warmup is not None else (3 if big else 200)
+    dev = torch.device("cuda", 0)
+
+    inp = W.make_workload(wl.name, seed=0)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    ncopies = max(1, -(-COPY_TARGET_BYTES // sz["weight"])) if not big else 1
+    w0 = B.W8A8Weight(to_dev(inp.qw), to_dev(inp.gscale),
+                      None if inp.rscale is None else to_dev(inp.rscale), inp.fmt)
+    weights = [w0] + [B.W8A8Weight(w0.codes.clone(), w0.gscale.clone(),
+                                   None if w0.rscale is None else w0.rscale.clone(), w0.fmt)
+                      for _ in range(ncopies - 1)]
+    x = to_dev(inp.x)
+    q = torch.empty((wl.M, wl.K), dtype=torch.int8, device=dev)
+    s = torch.empty((wl.M,), dtype=torch.float32, device=dev)
+    ys = [torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev) for _ in range(ncopies)]
+    contract = B.w8a8_gemm if big else B.w8a8_gemv
+
+    def step(i):
+        B.quant_act_i8(x, rotate=True, q=q, scale=s)
+        contract(q, s, weights[i], y=ys[i])
+
+    def contraction_only(i):
+        contract(q, s, weights[i], y=ys[i])
+
+    stream = torch.cuda.Stream(device=dev)             # default priority
+    torch.cuda.synchronize()
+
+    def make_round(fn):
+        """One round = one call per weight copy; graph-captured unless --eager."""
+        if args.eager:
+            def run():
+                for i in range(ncopies):
+                    fn(i)
+            return run
+        with torch.cuda.stream(stream):
+            for i in range(ncopies):                   # warm the code path before capture
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(ncopies):
+                fn(i)
+        torch.cuda.synchronize()
+        return g.replay
+
+    def timed(fn, n_calls, n_warm):
+        run = make_round(fn)
+        rounds = max(1, -(-n_calls // ncopies))
+        wrounds = max(1, -(-n_warm // ncopies)) if n_warm > 0 else 0
+        with torch.cuda.stream(stream):
+            for _ in range(wrounds):
+                run()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(rounds):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        ms = e0.elapsed_time(e1)
+        return ms / (rounds * ncopies), (t1 - t0) * 1e3 / (rounds * ncopies), rounds * ncopies
+
+    # ---- the whole step
+    ms_step, wall_ms_step, nsteps = timed(step, steps, warmup)
+    if big:
+        value = sz["ops"] / (ms_step * 1e-3) / 1e12
+        unit = "TOPS"
+    else:
+        value = sz["step"] / (ms_step * 1e-3) / 1e9
+        unit = "GB/s"
+
+    # ---- the dominant kernel alone (same stream, same launch configuration)
+    ms_k, _, _ = timed(contraction_only, steps, warmup)
+    if big:
+        achieved = sz["ops"] / (ms_k * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": INT8_PEAK_TOPS,
+                "unit": "TOPS", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    else:
+        achieved = sz["contraction"] / (ms_k * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = "rad_w8a8_gemm" if big else "rad_w8a8_gemv"
+    roof["us_per_launch"] = round(ms_k * 1e3, 3)
+    roof["traffic"] = load_traffic(wl.name)
+
+    # ---- parity of the timed buffers against the oracle (sampled rows)
+    import oracle
+    rows = np.arange(wl.M) if wl.M <= 4 else np.unique(np.linspace(0, wl.M - 1, 4).astype(int))
+    qo, so = oracle.quant_act_i8(inp.x[rows])
+    yo = oracle.linear(qo, so, inp.qw, wl.fmt, inp.gscale, inp.rscale)
+    parity = bool(np.array_equal(q.cpu().numpy()[rows], qo))
+    for y in ys:
+        yg = y.cpu().numpy()[rows].astype(np.float64)
+        nrm = np.linalg.norm(yo.astype(np.float64), axis=1)
+        err = np.max(np.abs(yg - yo), axis=1)
+        parity = parity and bool(np.all(err <= 1e-5 * nrm))
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu_rows = min(wl.M, 1 if not big else 16)
+        xs = inp.x[:cpu_rows]
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            qo, so = oracle.quant_act_i8(xs)
+            oracle.linear(qo, so, inp.qw, wl.fmt, inp.gscale, inp.rscale)
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - t0) / n
+        frac = cpu_rows / wl.M
+        if big:
+            cv = sz["ops"] * frac / dt / 1e12
+        else:
+            cv = (sz["step"] - (wl.M - cpu_rows) * (wl.K * 4 + wl.N * 4)) / dt / 1e9
+        cpu = {"value": round(cv, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "%d of %d tokens, whole weight, %d repetitions, %.1f s"
+                         % (cpu_rows, wl.M, n, dt * n)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": nsteps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
+                   "format": "u8g256_bf16row" if wl.fmt == W.FMT_U8G256_BF16ROW else "bf16g128",
+                   "weight_copies": ncopies, "launch": "eager" if args.eager else "hip_graph",
+                   "host_ms_per_step": round(wall_ms_step, 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_on_timed_buffers": parity,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

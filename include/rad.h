@@ -1,0 +1,168 @@
+/*
+ * rad.h -- C ABI of librad.so: the rotated W8A8 int8 linear layer on AMD
+ * MI355X (gfx950).
+ *
+ * The layer is the one on the model card "Qwen3.8-27B IQ8R + DFlash2 --
+ * radiance container":
+ *   - table row "Weights": trunk linears hold int8 codes in -127..127, one u8
+ *     scale for every (row, 256 of K) under one bf16 scale per row, and every
+ *     128 of K is rotated by the unnormalised Hadamard transform; the lm_head
+ *     holds int8 codes with one bf16 scale for every (row, 128 of K);
+ *   - table row "Activations": activations are int8 in the same rotated
+ *     domain (W8A8);
+ *   - section "How this file was made": the recipe rules that name these two
+ *     formats and the fwht128 transform.
+ * The card gives no code and no interface; the calls below are this
+ * library's own.
+ *
+ * Conventions for every call:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates nothing, keeps no pointer after it returns, and holds no state.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *     default stream) and returns without synchronising.  The caller keeps the
+ *     buffers alive until that stream's work completes.  Calls on different
+ *     streams may run concurrently; the library is thread-safe.
+ *   - Every argument is validated on the host BEFORE any HIP call, so a bad
+ *     argument returns an error status and enqueues nothing.  A HIP error
+ *     reported by the launch is returned as RAD_E_HIP.
+ *   - Sizes of zero (rows, M or N) are valid and enqueue nothing.
+ *   - Data values are not checked: NaN or infinite activations, and weight
+ *     codes of -128, give unspecified results.
+ *   - Layouts are row-major and dense (no strides).
+ */
+#ifndef RAD_H
+#define RAD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *rad_stream_t; /* hipStream_t */
+
+/* Status codes returned by every call. */
+enum rad_status {
+    RAD_OK = 0,
+    RAD_E_NULL = -1,   /* a required pointer is NULL                          */
+    RAD_E_SHAPE = -2,  /* a size is negative, or K is not a multiple of the
+                          rotation block (128) or of the format's group width */
+    RAD_E_ALIGN = -3,  /* a pointer is not aligned as the call requires       */
+    RAD_E_FMT = -4,    /* unknown weight format, or a scale pointer that the
+                          format requires is missing / forbids is present     */
+    RAD_E_RANGE = -5,  /* a size is beyond what the call supports             */
+    RAD_E_ALIAS = -6,  /* an output overlaps another argument                  */
+    RAD_E_HIP = -7     /* the HIP runtime reported an error at launch          */
+};
+
+/* Weight formats. */
+enum rad_format {
+    /* Trunk linears: codes int8 [N][K]; gscale uint8 [N][K/256] (a plain
+       integer multiplier per (row, 256 of K)); rscale bf16 bits [N]. */
+    RAD_FMT_U8G256_BF16ROW = 0,
+    /* Vocabulary head: codes int8 [N][K]; gscale bf16 bits [N][K/128];
+       rscale must be NULL. */
+    RAD_FMT_BF16G128 = 1
+};
+
+/* Largest K that rad_quant_act_i8 accepts (its rows are held on chip). */
+#define RAD_QUANT_MAX_K 65536
+/* Largest M that rad_w8a8_gemv accepts. */
+#define RAD_GEMV_MAX_M 128
+
+/*
+ * A quantised weight in the rotated domain.  Codes are int8 in -127..127 and
+ * each contiguous 128 of a row's K has already been rotated by H (the
+ * 128x128 Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j), no
+ * normalisation).  codes must be 16-byte aligned.  gscale and rscale have no
+ * alignment requirement.
+ */
+typedef struct rad_w8a8_weight {
+    const int8_t *codes;     /* int8 [N][K]                                   */
+    const void *gscale;      /* see enum rad_format                           */
+    const uint16_t *rscale;  /* bf16 bits [N], or NULL for RAD_FMT_BF16G128    */
+    int64_t N;               /* output features                               */
+    int64_t K;               /* input features                                */
+    int32_t fmt;             /* enum rad_format                               */
+} rad_w8a8_weight;
+
+/*
+ * rad_fwht128 -- y = x rotated block by block: each contiguous 128 of a row
+ * of x is multiplied by H (model card, table row "Weights": every 128 of K is
+ * rotated by the unnormalised Hadamard transform; table row "Activations":
+ * the same rotation applies to activations).
+ *
+ *   x, y   f32 [rows][K], 16-byte aligned.  y == x (in place) is allowed; any
+ *          other overlap returns RAD_E_ALIAS.
+ *   rows   >= 0.  K > 0 and K % 128 == 0.
+ *
+ * The f32 result is the butterfly network with stage widths 1, 2, 4, ..., 64
+ * in that order, the sum of each butterfly going to the lower index and the
+ * difference (lower minus upper) to the upper; it equals x.H exactly whenever
+ * no partial sum rounds.
+ */
+int rad_fwht128(const float *x, float *y, int64_t rows, int64_t K, rad_stream_t stream);
+
+/*
+ * rad_quant_act_i8 -- per-token symmetric int8 quantisation of activations,
+ * optionally rotated first (model card, table row "Activations": int8 under
+ * the same rotation as the weights; codes are symmetric in -127..127 as the
+ * weights' are, table row "Weights").
+ *
+ *   x      f32 [M][K], 16-byte aligned.
+ *   q      int8 [M][K] output, 16-byte aligned.
+ *   scale  f32 [M] output, 4-byte aligned.
+ *   rotate 1: x~ = x rotated as by rad_fwht128 (bit-identical); 0: x~ = x.
+ *   M >= 0; K > 0, K % 128 == 0, K <= RAD_QUANT_MAX_K.
+ *
+ * Per token m: amax = max_k |x~[m][k]|; scale[m] = amax / 127 (f32 division);
+ * q[m][k] = clamp(rne(x~[m][k] / scale[m]), -127, 127) with an f32 division and
+ * ties to even.  amax == 0 gives scale[m] = 0 and q[m][:] = 0.  No output may
+ * overlap x or the other output (RAD_E_ALIAS).
+ */
+int rad_quant_act_i8(const float *x, int8_t *q, float *scale, int64_t M, int64_t K, int rotate,
+                     rad_stream_t stream);
+
+/*
+ * rad_w8a8_gemv -- the rotated W8A8 contraction and epilogue for decode and
+ * verify sized batches, 1 <= M <= RAD_GEMV_MAX_M (model card, table row
+ * "Weights": int8 codes under a u8 scale per (row, 256 of K) and a bf16 row
+ * scale, or for the lm_head a bf16 scale per (row, 128 of K); table row
+ * "Activations": int8 activations in the same rotated domain).
+ *
+ *   q         int8 [M][K] activation codes (from rad_quant_act_i8), 16-byte aligned.
+ *   scale     f32 [M] activation scales.
+ *   w         host pointer to the weight descriptor (its fields point to device
+ *             memory); w->K is the K of q.
+ *   y         f32 [M][N] output, 4-byte aligned.
+ *   partials  NULL, or int32 [M][N][G] output (G = K / group width, 4-byte
+ *             aligned) that receives every group partial; a debug aid, slower.
+ *
+ * P[m][n][g] = sum over the K indices k of group g of q[m][k] * codes[n][k]
+ * (exact int32).  Output:
+ *   RAD_FMT_U8G256_BF16ROW: y = scale[m] * r[n] * 2^-7 * sum_g u8[n][g] * P[m][n][g]
+ *   RAD_FMT_BF16G128:       y = scale[m] * 2^-7 * sum_g b[n][g] * P[m][n][g]
+ * 2^-7 undoes H.H^T = 128 I, since both operands were rotated.  The f32 sum
+ * order of the epilogue is unspecified.  M > RAD_GEMV_MAX_M returns
+ * RAD_E_RANGE.  y and partials may not overlap each other or any input.
+ */
+int rad_w8a8_gemv(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
+                  int64_t M, int32_t *partials, rad_stream_t stream);
+
+/*
+ * rad_w8a8_gemm -- the same contraction and epilogue as rad_w8a8_gemv for any
+ * M >= 0 (prefill sized batches), on int8 matrix cores.  Same arguments,
+ * layouts and errors, without the limit on M.  For equal inputs both calls
+ * produce identical partials.
+ */
+int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
+                  int64_t M, int32_t *partials, rad_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *rad_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAD_H */

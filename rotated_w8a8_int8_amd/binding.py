@@ -1,0 +1,213 @@
+"""ctypes binding of librad.so (include/rad.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  PyTorch supplies device memory (tensors) and the stream each call is
+enqueued on (the current stream of the tensors' device).  Nothing here falls
+back to another implementation: if the library is not built, or a tensor is
+not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librad.so")
+
+# enum rad_status
+RAD_OK = 0
+RAD_E_NULL = -1
+RAD_E_SHAPE = -2
+RAD_E_ALIGN = -3
+RAD_E_FMT = -4
+RAD_E_RANGE = -5
+RAD_E_ALIAS = -6
+RAD_E_HIP = -7
+# enum rad_format
+RAD_FMT_U8G256_BF16ROW = 0
+RAD_FMT_BF16G128 = 1
+GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128}
+RAD_QUANT_MAX_K = 65536
+RAD_GEMV_MAX_M = 128
+
+EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_strerror")
+
+
+class RadError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (call, strerror(status), status))
+
+
+class WeightDesc(ctypes.Structure):
+    """struct rad_w8a8_weight."""
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("gscale", ctypes.c_void_p),
+        ("rscale", ctypes.c_void_p),
+        ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("fmt", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Open librad.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("librad.so is not built; run `python -m rotated_w8a8_int8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.rad_fwht128.argtypes = [vp, vp, i64, i64, vp]
+        L.rad_quant_act_i8.argtypes = [vp, vp, vp, i64, i64, ci, vp]
+        L.rad_w8a8_gemv.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
+        L.rad_w8a8_gemm.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
+        for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm):
+            f.restype = ci
+        L.rad_strerror.argtypes = [ci]
+        L.rad_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().rad_strerror(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != RAD_OK:
+        raise RadError(status, call)
+
+
+# ---------------------------------------------------------------- tensors --
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(t):
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+@dataclass
+class W8A8Weight:
+    """Device tensors of one quantised weight in the rotated domain.
+
+    codes  int8 [N][K]
+    gscale uint8 [N][K/256] (RAD_FMT_U8G256_BF16ROW) or int16/uint16 bf16 bits [N][K/128]
+    rscale int16/uint16 bf16 bits [N] for RAD_FMT_U8G256_BF16ROW, else None
+    """
+    codes: object
+    gscale: object
+    rscale: object
+    fmt: int
+
+    @property
+    def N(self) -> int:
+        return int(self.codes.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.codes.shape[1])
+
+    def desc(self) -> WeightDesc:
+        torch = _torch()
+        _dev(self.codes, torch.int8, "codes")
+        if self.fmt == RAD_FMT_U8G256_BF16ROW:
+            _dev(self.gscale, torch.uint8, "gscale")
+        elif self.gscale.dtype not in (torch.int16, torch.uint16):
+            raise TypeError("gscale must hold bf16 bits (int16/uint16)")
+        if self.rscale is not None and self.rscale.dtype not in (torch.int16, torch.uint16):
+            raise TypeError("rscale must hold bf16 bits (int16/uint16)")
+        return WeightDesc(self.codes.data_ptr(), self.gscale.data_ptr(),
+                          None if self.rscale is None else self.rscale.data_ptr(),
+                          self.N, self.K, self.fmt)
+
+
+def fwht128(x, out=None):
+    """Rotate each contiguous 128-block of the last dim of f32 ``x`` (``out`` may be ``x``)."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    K = x.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, torch.float32, "out")
+    rows = x.numel() // K if K else 0
+    _check(lib().rad_fwht128(x.data_ptr(), out.data_ptr(), rows, K, _stream(x)), "rad_fwht128")
+    return out
+
+
+def quant_act_i8(x, rotate: bool = True, q=None, scale=None):
+    """Per-token int8 codes and f32 scales of f32 ``x`` [M][K]."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    _check(lib().rad_quant_act_i8(x.data_ptr(), q.data_ptr(), scale.data_ptr(), M, K,
+                                  1 if rotate else 0, _stream(x)), "rad_quant_act_i8")
+    return q, scale
+
+
+def _linear_call(fn, name, q, scale, w: W8A8Weight, y, partials):
+    torch = _torch()
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    M = int(q.shape[0])
+    if q.shape[1] != w.K:
+        raise ValueError("q has K=%d, weight has K=%d" % (q.shape[1], w.K))
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float32, device=q.device)
+    _dev(y, torch.float32, "y")
+    pp = None
+    if partials is True:
+        partials = torch.empty((M, w.N, w.K // GROUP_WIDTH[w.fmt]), dtype=torch.int32, device=q.device)
+    if partials is not None and partials is not False:
+        _dev(partials, torch.int32, "partials")
+        pp = partials.data_ptr()
+    else:
+        partials = None
+    d = w.desc()
+    _check(fn(q.data_ptr(), scale.data_ptr(), ctypes.byref(d), y.data_ptr(), M, pp, _stream(q)), name)
+    return y, partials
+
+
+def w8a8_gemv(q, scale, w: W8A8Weight, y=None, partials=None):
+    """y [M][N] (and optionally the int32 group partials) for 1 <= M <= 128."""
+    return _linear_call(lib().rad_w8a8_gemv, "rad_w8a8_gemv", q, scale, w, y, partials)
+
+
+def w8a8_gemm(q, scale, w: W8A8Weight, y=None, partials=None):
+    """y [M][N] (and optionally the int32 group partials) for any M."""
+    return _linear_call(lib().rad_w8a8_gemm, "rad_w8a8_gemm", q, scale, w, y, partials)
+
+
+def linear(x, w: W8A8Weight):
+    """The whole layer on f32 activations: rotate + quantise, then contract."""
+    q, s = quant_act_i8(x, rotate=True)
+    if q.shape[0] <= RAD_GEMV_MAX_M:
+        y, _ = w8a8_gemv(q, s, w)
+    else:
+        y, _ = w8a8_gemm(q, s, w)
+    return y

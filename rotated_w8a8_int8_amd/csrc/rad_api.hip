@@ -1,0 +1,125 @@
+// rad_api.hip -- the C ABI of librad.so (declared in include/rad.h).
+//
+// Every call validates all of its arguments on the host before touching the
+// HIP runtime, then enqueues its kernels on the caller's stream.  Check order:
+// descriptor present -> format -> shapes -> ranges -> (empty: done) ->
+// pointers -> alignment -> aliasing.
+#include <stdint.h>
+
+#include "../../include/rad.h"
+#include "rad_launch.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Span span(const void *p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+constexpr int64_t kI32Max = 2147483647;
+
+int group_width(int32_t fmt) {
+    if (fmt == RAD_FMT_U8G256_BF16ROW) return 256;
+    if (fmt == RAD_FMT_BF16G128) return 128;
+    return 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RAD_OK : RAD_E_HIP; }
+
+// Shared validation of the two contraction entry points.
+int check_linear(const int8_t *q, const float *scale, const rad_w8a8_weight *w, const float *y,
+                 int64_t M, const int32_t *partials, int64_t max_m) {
+    if (!w) return RAD_E_NULL;
+    const int gw = group_width(w->fmt);
+    if (gw == 0) return RAD_E_FMT;
+    if (w->fmt == RAD_FMT_U8G256_BF16ROW && !w->rscale) return RAD_E_FMT;
+    if (w->fmt == RAD_FMT_BF16G128 && w->rscale) return RAD_E_FMT;
+    if (M < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
+    if (M > max_m || w->N > kI32Max || w->K > kI32Max) return RAD_E_RANGE;
+    if (M == 0 || w->N == 0) return 1;  // nothing to do
+    if (!q || !scale || !y || !w->codes || !w->gscale) return RAD_E_NULL;
+    if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(scale, 4) || !aligned(y, 4) ||
+        (partials && !aligned(partials, 4)))
+        return RAD_E_ALIGN;
+    const int64_t N = w->N, K = w->K, G = K / gw;
+    const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
+    const Span in[] = {span(q, M * K), span(scale, M * 4), span(w->codes, N * K),
+                       span(w->gscale, N * G * esz),
+                       w->rscale ? span(w->rscale, N * 2) : Span{0, 0}};
+    const Span ys = span(y, M * N * 4);
+    const Span ps = partials ? span(partials, M * N * G * 4) : Span{0, 0};
+    for (const Span &s : in) {
+        if (overlap(ys, s)) return RAD_E_ALIAS;
+        if (partials && overlap(ps, s)) return RAD_E_ALIAS;
+    }
+    if (partials && overlap(ys, ps)) return RAD_E_ALIAS;
+    return RAD_OK;
+}
+
+rad::WeightArgs weight_args(const rad_w8a8_weight *w) {
+    return rad::WeightArgs{w->codes, w->gscale, w->rscale, w->N, w->K, static_cast<int>(w->fmt)};
+}
+
+}  // namespace
+
+extern "C" {
+
+int rad_fwht128(const float *x, float *y, int64_t rows, int64_t K, rad_stream_t stream) {
+    if (rows < 0 || K <= 0 || K % 128 != 0) return RAD_E_SHAPE;
+    if (rows > 0 && K > INT64_MAX / 4 / rows) return RAD_E_RANGE;
+    if (rows == 0) return RAD_OK;
+    if (!x || !y) return RAD_E_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return RAD_E_ALIGN;
+    if (x != y && overlap(span(x, rows * K * 4), span(y, rows * K * 4))) return RAD_E_ALIAS;
+    return hip_status(rad::launch_fwht128(x, y, rows, K, static_cast<hipStream_t>(stream)));
+}
+
+int rad_quant_act_i8(const float *x, int8_t *q, float *scale, int64_t M, int64_t K, int rotate,
+                     rad_stream_t stream) {
+    if (M < 0 || K <= 0 || K % 128 != 0) return RAD_E_SHAPE;
+    if (K > RAD_QUANT_MAX_K || M > kI32Max || (rotate != 0 && rotate != 1)) return RAD_E_RANGE;
+    if (M == 0) return RAD_OK;
+    if (!x || !q || !scale) return RAD_E_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return RAD_E_ALIGN;
+    const Span xs = span(x, M * K * 4), qs = span(q, M * K), ss = span(scale, M * 4);
+    if (overlap(xs, qs) || overlap(xs, ss) || overlap(qs, ss)) return RAD_E_ALIAS;
+    return hip_status(rad::launch_quant_act(x, q, scale, M, K, rotate, static_cast<hipStream_t>(stream)));
+}
+
+int rad_w8a8_gemv(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
+                  int64_t M, int32_t *partials, rad_stream_t stream) {
+    const int rc = check_linear(q, scale, w, y, M, partials, RAD_GEMV_MAX_M);
+    if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
+    return hip_status(rad::launch_gemv(q, scale, weight_args(w), y, M, partials,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
+                  int64_t M, int32_t *partials, rad_stream_t stream) {
+    const int rc = check_linear(q, scale, w, y, M, partials, kI32Max);
+    if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
+    return hip_status(rad::launch_gemm(q, scale, weight_args(w), y, M, partials,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+const char *rad_strerror(int status) {
+    switch (status) {
+        case RAD_OK: return "success";
+        case RAD_E_NULL: return "a required pointer is NULL";
+        case RAD_E_SHAPE: return "invalid shape (negative size, or K not a multiple of 128 / the group width)";
+        case RAD_E_ALIGN: return "a pointer is not aligned as required";
+        case RAD_E_FMT: return "unknown weight format or wrong scale pointers for the format";
+        case RAD_E_RANGE: return "a size or flag is beyond what the call supports";
+        case RAD_E_ALIAS: return "an output overlaps another argument";
+        case RAD_E_HIP: return "the HIP runtime reported an error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// rad_device.h -- device helpers shared by the librad kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rad {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> f32 (a bf16 is the high half of an f32; exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// ---- DPP lane exchanges inside one 16-lane row --------------------------
+// Each returns the value held by lane (lane ^ X) of the same row.  xor 1 and
+// xor 2 are single quad permutations; xor 4 and xor 8 compose a mirror with a
+// second permutation (half-mirror maps i -> i^7, mirror maps i -> i^15).
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kQuadXor3 = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kRowMirror = 0x140;      // lane i <- 15 - i
+constexpr int kRowHalfMirror = 0x141;  // lane i <- i ^ 7
+
+__device__ __forceinline__ int lane_xor1(int v) { return dpp<kQuadXor1>(v); }
+__device__ __forceinline__ int lane_xor2(int v) { return dpp<kQuadXor2>(v); }
+__device__ __forceinline__ int lane_xor4(int v) { return dpp<kQuadXor3>(dpp<kRowHalfMirror>(v)); }
+__device__ __forceinline__ int lane_xor8(int v) { return dpp<kRowHalfMirror>(dpp<kRowMirror>(v)); }
+
+template <int X>
+__device__ __forceinline__ int lane_xor(int v) {
+    static_assert(X == 1 || X == 2 || X == 4 || X == 8, "xor inside a 16-lane row");
+    if constexpr (X == 1) return lane_xor1(v);
+    else if constexpr (X == 2) return lane_xor2(v);
+    else if constexpr (X == 4) return lane_xor4(v);
+    else return lane_xor8(v);
+}
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+    return __int_as_float(lane_xor<X>(__float_as_int(v)));
+}
+
+// Exact integer sum over the 16 lanes of each DPP row (every lane gets it).
+__device__ __forceinline__ int row16_sum(int v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<8>(v);
+    return v;
+}
+// Exact integer sum over the 8 lanes of each half row.
+__device__ __forceinline__ int row8_sum(int v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    return v;
+}
+
+// Wave-uniform sum of an int over all 64 lanes (result in a scalar register).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+    v = row16_sum(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Wave-uniform f32 sum (order fixed: 16-lane butterflies, then rows 0+1+2+3).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    v += lane_xor<4>(v);
+    v += lane_xor<8>(v);
+    float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, lane_xor<1>(v));
+    v = fmaxf(v, lane_xor<2>(v));
+    v = fmaxf(v, lane_xor<4>(v));
+    v = fmaxf(v, lane_xor<8>(v));
+    float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// 4 x int8 dot products of a 16-byte chunk pair, exact int32.
+__device__ __forceinline__ int dot16_i8(v4i a, v4i b, int acc) {
+    acc = __builtin_amdgcn_sdot4(a.x, b.x, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.y, b.y, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
+    acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
+    return acc;
+}
+
+// Loads that bypass nothing: plain 16-byte global loads.
+__device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
+
+}  // namespace rad

@@ -1,0 +1,27 @@
+// rad_launch.h -- host-side launchers of the librad kernels.  Arguments are
+// already validated by rad_api.cpp; each launcher enqueues on `st` and returns
+// the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rad {
+
+struct WeightArgs {
+    const int8_t *codes;     // int8 [N][K]
+    const void *gscale;      // u8 [N][K/256] or bf16 bits [N][K/128]
+    const uint16_t *rscale;  // bf16 bits [N] (u8 format) or nullptr
+    int64_t N, K;
+    int fmt;                 // 0: u8 per 256 + bf16 row; 1: bf16 per 128
+};
+
+hipError_t launch_fwht128(const float *x, float *y, int64_t rows, int64_t K, hipStream_t st);
+hipError_t launch_quant_act(const float *x, int8_t *q, float *s, int64_t M, int64_t K, int rotate,
+                            hipStream_t st);
+hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
+                       int32_t *partials, hipStream_t st);
+hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
+                       int32_t *partials, hipStream_t st);
+
+}  // namespace rad

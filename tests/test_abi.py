@@ -1,0 +1,131 @@
+"""The C ABI on the host: the library loads, exports what include/rad.h declares,
+and every entry point rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel: each one either fails validation or has an
+empty size, both of which return before any HIP call.  Fake, never
+dereferenced addresses stand in for device pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rotated_w8a8_int8_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rad.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="librad.so not built")
+
+A = 0x7F0000000000          # fake, 256-byte aligned device addresses, far apart
+Bp = 0x7F1000000000
+C = 0x7F2000000000
+D = 0x7F3000000000
+E = 0x7F4000000000
+F = 0x7F5000000000
+NULLS = 0
+
+
+def header_text():
+    return open(HEADER).read()
+
+
+def test_exports_every_declared_function():
+    decl = set(re.findall(r"^(?:int|const char \*)\s*(rad_\w+)\(", header_text(), re.M))
+    assert decl == set(B.EXPORTS)
+    L = B.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_constants_match_header():
+    h = header_text()
+    for name in ("RAD_OK", "RAD_E_NULL", "RAD_E_SHAPE", "RAD_E_ALIGN", "RAD_E_FMT",
+                 "RAD_E_RANGE", "RAD_E_ALIAS", "RAD_E_HIP", "RAD_FMT_U8G256_BF16ROW",
+                 "RAD_FMT_BF16G128"):
+        m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, h)
+        assert m and int(m.group(1)) == getattr(B, name), name
+    for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M"):
+        m = re.search(r"#define %s (\d+)" % name, h)
+        assert m and int(m.group(1)) == getattr(B, name)
+
+
+def test_strerror_never_null():
+    for s in range(-9, 2):
+        assert isinstance(B.strerror(s), str) and B.strerror(s)
+
+
+# ------------------------------------------------------------- fwht128 --
+
+def test_fwht_validation():
+    f = B.lib().rad_fwht128
+    assert f(A, Bp, 4, 100, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, -1, 128, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, 4, 0, None) == B.RAD_E_SHAPE
+    assert f(NULLS, Bp, 4, 128, None) == B.RAD_E_NULL
+    assert f(A, NULLS, 4, 128, None) == B.RAD_E_NULL
+    assert f(A + 4, Bp, 4, 128, None) == B.RAD_E_ALIGN
+    assert f(A, A + 512, 4, 128, None) == B.RAD_E_ALIAS          # partial overlap
+    assert f(NULLS, NULLS, 0, 128, None) == B.RAD_OK              # empty: nothing enqueued
+    assert f(A, Bp, 1 << 40, 1 << 40, None) == B.RAD_E_RANGE
+
+
+# --------------------------------------------------------------- quant --
+
+def test_quant_validation():
+    f = B.lib().rad_quant_act_i8
+    assert f(A, Bp, C, 2, 200, 1, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, C, -2, 256, 1, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, C, 2, B.RAD_QUANT_MAX_K + 128, 1, None) == B.RAD_E_RANGE
+    assert f(A, Bp, C, 2, 256, 2, None) == B.RAD_E_RANGE           # rotate must be 0 or 1
+    assert f(NULLS, Bp, C, 2, 256, 1, None) == B.RAD_E_NULL
+    assert f(A, NULLS, C, 2, 256, 1, None) == B.RAD_E_NULL
+    assert f(A, Bp, NULLS, 2, 256, 1, None) == B.RAD_E_NULL
+    assert f(A + 8, Bp, C, 2, 256, 1, None) == B.RAD_E_ALIGN
+    assert f(A, Bp + 4, C, 2, 256, 1, None) == B.RAD_E_ALIGN
+    assert f(A, Bp, C + 2, 2, 256, 1, None) == B.RAD_E_ALIGN
+    assert f(A, A + 1024, C, 2, 256, 1, None) == B.RAD_E_ALIAS     # q inside x
+    assert f(A, Bp, Bp + 256, 2, 256, 1, None) == B.RAD_E_ALIAS    # scale inside q
+    assert f(NULLS, NULLS, NULLS, 0, 256, 1, None) == B.RAD_OK
+
+
+# ---------------------------------------------------------- contraction --
+
+def desc(fmt=B.RAD_FMT_U8G256_BF16ROW, N=64, K=512, codes=C, gscale=D, rscale=E):
+    return B.WeightDesc(codes, gscale, rscale, N, K, fmt)
+
+
+@pytest.mark.parametrize("name,max_m", [("rad_w8a8_gemv", B.RAD_GEMV_MAX_M), ("rad_w8a8_gemm", None)])
+def test_linear_validation(name, max_m):
+    f = getattr(B.lib(), name)
+
+    def call(d, M=4, q=A, s=Bp, y=F, p=None):
+        return f(q, s, None if d is None else ctypes.byref(d), y, M, p, None)
+
+    assert call(None) == B.RAD_E_NULL
+    assert call(desc(fmt=7)) == B.RAD_E_FMT
+    assert call(desc(rscale=None)) == B.RAD_E_FMT                   # u8 format needs row scales
+    assert call(desc(fmt=B.RAD_FMT_BF16G128)) == B.RAD_E_FMT        # head format forbids them
+    assert call(desc(K=384)) == B.RAD_E_SHAPE                       # K % 256 for the u8 format
+    assert call(desc(K=200, fmt=B.RAD_FMT_BF16G128, rscale=None)) == B.RAD_E_SHAPE
+    assert call(desc(N=-1)) == B.RAD_E_SHAPE
+    assert call(desc(), M=-1) == B.RAD_E_SHAPE
+    if max_m is not None:
+        assert call(desc(), M=max_m + 1) == B.RAD_E_RANGE
+    assert call(desc(N=1 << 31)) == B.RAD_E_RANGE
+    assert call(desc(), M=0, q=0, s=0, y=0) == B.RAD_OK              # empty batch
+    assert call(desc(N=0, codes=0, gscale=0), q=0, s=0, y=0) == B.RAD_OK
+    assert call(desc(), q=0) == B.RAD_E_NULL
+    assert call(desc(), s=0) == B.RAD_E_NULL
+    assert call(desc(), y=0) == B.RAD_E_NULL
+    assert call(desc(codes=0)) == B.RAD_E_NULL
+    assert call(desc(gscale=0)) == B.RAD_E_NULL
+    assert call(desc(), q=A + 4) == B.RAD_E_ALIGN
+    assert call(desc(codes=C + 8)) == B.RAD_E_ALIGN
+    assert call(desc(), y=F + 2) == B.RAD_E_ALIGN
+    assert call(desc(), p=F + 0x100000 + 1) == B.RAD_E_ALIGN
+    assert call(desc(), y=A + 16) == B.RAD_E_ALIAS                  # y over q
+    assert call(desc(), y=C + 4096) == B.RAD_E_ALIAS                # y over codes
+    assert call(desc(), p=D) == B.RAD_E_ALIAS                       # partials over gscale
+    assert call(desc(), p=F + 64) == B.RAD_E_ALIAS                  # partials over y

@@ -1,0 +1,255 @@
+"""GPU parity: librad.so (through its C ABI) against the CPU oracle.
+
+Bar: rotated activations, int8 codes, activation scales and int32 group
+partials bit-exact; f32 outputs within 1e-5 of the oracle per output row,
+measured as max_n |y - y_ref| / ||y_ref[m, :]||_2 (a row whose reference is all
+zero must come out all zero).  The oracle's f64 epilogue differs from any f32
+evaluation order by far less: an f32 sum of at most a few hundred scaled
+partials carries a relative error near 1e-7 of the row norm.
+
+Small shapes span several tiles with ragged tails and are compared in full.
+The five workloads are run at full size in the launch configuration the
+benchmark uses; their codes are compared in full and their partials and
+outputs on sampled token rows that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from rotated_w8a8_int8_amd import binding as B
+from rotated_w8a8_int8_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    return _t
+
+
+def dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def weight(torch, inp):
+    return B.W8A8Weight(dev(torch, inp.qw), dev(torch, inp.gscale),
+                        None if inp.rscale is None else dev(torch, inp.rscale), inp.fmt)
+
+
+def assert_rows_close(y, ref, tol=TOL):
+    y = y.astype(np.float64)
+    ref = ref.astype(np.float64)
+    nrm = np.linalg.norm(ref, axis=1)
+    err = np.max(np.abs(y - ref), axis=1) if y.shape[1] else np.zeros(len(y))
+    zero = nrm == 0
+    assert np.all(y[zero] == 0)
+    rel = err[~zero] / nrm[~zero]
+    assert rel.size == 0 or rel.max() <= tol, "max row-relative error %.3g" % rel.max()
+
+
+# --------------------------------------------------------------- rotation --
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (3, 384), (5, 1024), (7, 5120), (33, 17408), (1001, 256)])
+def test_fwht_bit_exact(torch, rows, K):
+    x = W.make(rows, K, 1, W.FMT_BF16G128, seed=rows + K).x
+    ref = oracle.fwht128(x)
+    xd = dev(torch, x)
+    got = host(B.fwht128(xd))
+    assert np.array_equal(got.view(np.int32), ref.view(np.int32))
+    B.fwht128(xd, out=xd)                                   # in place
+    assert np.array_equal(host(xd).view(np.int32), ref.view(np.int32))
+
+
+def test_fwht_integer_inputs_exact_hadamard(torch):
+    import scipy.linalg
+    rng = np.random.default_rng(0)
+    x = rng.integers(-(1 << 16), 1 << 16, size=(5, 640)).astype(np.float32)
+    got = host(B.fwht128(dev(torch, x))).astype(np.int64)
+    H = scipy.linalg.hadamard(128).astype(np.int64)
+    want = (x.astype(np.int64).reshape(5, 5, 128) @ H).reshape(5, 640)
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------ quantisation --
+
+QUANT_SHAPES = [(1, 128), (1, 5120), (2, 384), (17, 1024), (3, 17408), (300, 5120), (260, 17408),
+                (1, 65536), (2, 32768)]
+
+
+@pytest.mark.parametrize("M,K", QUANT_SHAPES)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_quant_bit_exact(torch, M, K, rotate):
+    x = W.make(M, K, 1, W.FMT_BF16G128, seed=M * 7 + K).x
+    if M > 2:
+        x[1] = 0.0                                          # zero token
+        x[2] = 0.0
+        x[2, K // 2] = -3.25                                # a single nonzero
+    qr, sr = oracle.quant_act_i8(x, rotate=rotate)
+    q, s = B.quant_act_i8(dev(torch, x), rotate=rotate)
+    assert np.array_equal(host(s).view(np.int32), sr.view(np.int32))
+    assert np.array_equal(host(q), qr)
+
+
+def test_quant_ties_closed_form(torch):
+    # blocks of constant 128c rotate to (128c, 0, ...); with amax 127 the scale
+    # is 1 and halves round to even: -63.5 -> -64, 62.5 -> 62, 0.5 -> 0, 1.5 -> 2
+    vals = [127.0, -63.5, 62.5, 0.5, 1.5, -2.5]
+    x = np.zeros((1, 128 * len(vals)), np.float32)
+    for b, v in enumerate(vals):
+        x[0, 128 * b:128 * (b + 1)] = np.float32(v / 128)
+    q, s = B.quant_act_i8(dev(torch, x))
+    assert host(s)[0] == 1.0
+    assert list(host(q)[0, ::128]) == [127, -64, 62, 0, 2, -2]
+
+
+# ------------------------------------------------------------- contraction --
+
+def run_linear(torch, fn, inp, M_rows=None, with_partials=True):
+    q, s = oracle.quant_act_i8(inp.x)
+    w = weight(torch, inp)
+    qd, sd = dev(torch, q), dev(torch, s)
+    y, P = fn(qd, sd, w, partials=True if with_partials else None)
+    return q, s, host(y), (host(P) if with_partials else None), (qd, sd, w)
+
+
+SMALL = [
+    # (M, K, N, fmt)
+    (1, 512, 256, 0), (4, 512, 256, 0), (1, 256, 1, 0), (1, 1280, 77, 0), (1, 640, 33, 1),
+    (1, 3072, 300, 1), (2, 512, 65, 0), (16, 768, 130, 1), (17, 512, 100, 0), (33, 1024, 200, 1),
+    (64, 512, 63, 0), (128, 256, 64, 0), (100, 640, 129, 1), (3, 16384, 40, 0), (1, 33024, 20, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,fmt", SMALL)
+def test_gemv_small_shapes(torch, M, K, N, fmt):
+    inp = W.make(M, K, N, fmt, seed=M + K + N)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+    Pr = oracle.group_partials(q, inp.qw, fmt)
+    yr = oracle.epilogue(Pr, s, fmt, inp.gscale, inp.rscale)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, yr)
+    y2, _ = B.w8a8_gemv(qd, sd, w)                          # production path, no partials
+    assert np.array_equal(host(y2), y)
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [31, 32, 33, 47, 63, 64, 65, 80, 96, 100, 127, 128])
+def test_gemv_m_sweep(torch, M):
+    inp = W.make(M, 512, 96, 0, seed=1000 + M)
+    q, s, y, P, _ = run_linear(torch, B.w8a8_gemv, inp)
+    Pr = oracle.group_partials(q, inp.qw, 0)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, 0, inp.gscale, inp.rscale))
+
+
+def test_gemv_m1_u8_output_is_exact(torch):
+    # the M = 1 path sums u8 * P exactly and applies s * r * 2^-7 in f64 in the
+    # oracle's order, so its output equals the oracle's bit for bit
+    inp = W.make(1, 5120, 999, 0, seed=5)
+    q, s, y, _, _ = run_linear(torch, B.w8a8_gemv, inp, with_partials=False)
+    yr = oracle.linear(q, s, inp.qw, 0, inp.gscale, inp.rscale)
+    assert np.array_equal(y.view(np.int32), yr.view(np.int32))
+
+
+GEMM_SMALL = [
+    (1, 256, 16, 0), (5, 512, 256, 0), (130, 512, 130, 0), (257, 768, 300, 1), (128, 1024, 128, 0),
+    (200, 256, 33, 0), (300, 640, 70, 1), (129, 2048, 257, 0),
+]
+
+
+@pytest.mark.parametrize("M,K,N,fmt", GEMM_SMALL)
+def test_gemm_small_shapes(torch, M, K, N, fmt):
+    inp = W.make(M, K, N, fmt, seed=M * 3 + K + N)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemm, inp)
+    Pr = oracle.group_partials(q, inp.qw, fmt)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, fmt, inp.gscale, inp.rscale))
+    y2, _ = B.w8a8_gemm(qd, sd, w)
+    assert np.array_equal(host(y2), y)
+
+
+@pytest.mark.parametrize("M", [1, 15, 16, 17, 127, 128, 129, 255, 256, 257])
+def test_gemm_m_sweep(torch, M):
+    inp = W.make(M, 512, 136, 0, seed=2000 + M)
+    q, s, y, P, _ = run_linear(torch, B.w8a8_gemm, inp)
+    Pr = oracle.group_partials(q, inp.qw, 0)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, 0, inp.gscale, inp.rscale))
+
+
+@pytest.mark.parametrize("M,fmt", [(1, 0), (7, 1), (64, 0), (128, 1)])
+def test_gemv_and_gemm_give_identical_partials(torch, M, fmt):
+    inp = W.make(M, 1024, 200, fmt, seed=M)
+    _, _, _, P1, _ = run_linear(torch, B.w8a8_gemv, inp)
+    _, _, _, P2, _ = run_linear(torch, B.w8a8_gemm, inp)
+    assert np.array_equal(P1, P2)
+
+
+def test_empty_sizes_are_no_ops(torch):
+    inp = W.make(1, 512, 8, 0, seed=0)
+    w = weight(torch, inp)
+    q = torch.zeros((0, 512), dtype=torch.int8, device="cuda")
+    s = torch.zeros((0,), dtype=torch.float32, device="cuda")
+    y, _ = B.w8a8_gemv(q, s, w)
+    assert y.shape == (0, 8)
+    y, _ = B.w8a8_gemm(q, s, w)
+    assert y.shape == (0, 8)
+    qq, ss = B.quant_act_i8(torch.zeros((0, 256), dtype=torch.float32, device="cuda"))
+    assert qq.shape == (0, 256)
+
+
+def test_repeatable(torch):
+    inp = W.make(64, 1024, 300, 0, seed=3)
+    _, _, y1, P1, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+    for _ in range(3):
+        y2, P2 = B.w8a8_gemv(qd, sd, w, partials=True)
+        assert np.array_equal(host(y2), y1) and np.array_equal(host(P2), P1)
+
+
+# ------------------------------------------------------ full-size workloads --
+
+def sample_rows(M, n, seed):
+    if M <= n:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    pick = set([0, M - 1, M // 2]) | set(rng.choice(M, size=n, replace=False).tolist())
+    return np.array(sorted(pick))[:n + 3]
+
+
+@pytest.mark.parametrize("name,fn,nsample", [
+    ("tiny", "gemv", 4), ("decode_gate_up", "gemv", 1), ("verify_skinny", "gemv", 12),
+    ("vocab_head", "gemv", 6), ("prefill_down", "gemm", 10), ("tiny", "gemm", 4),
+])
+def test_workload_full_size(torch, name, fn, nsample):
+    wl = W.WORKLOADS[name]
+    print("workload", name, fn, flush=True)
+    inp = W.make_workload(name, seed=0)
+    xd = dev(torch, inp.x)
+    qd, sd = B.quant_act_i8(xd)
+    q, s = oracle.quant_act_i8(inp.x)
+    assert np.array_equal(host(sd).view(np.int32), s.view(np.int32))
+    assert np.array_equal(host(qd), q)
+    del xd
+    w = weight(torch, inp)
+    call = B.w8a8_gemv if fn == "gemv" else B.w8a8_gemm
+    y, P = call(qd, sd, w, partials=True)
+    rows = sample_rows(wl.M, nsample, seed=1)
+    rows_t = torch.from_numpy(rows).cuda()
+    Ps = host(P.index_select(0, rows_t))
+    ys = host(y.index_select(0, rows_t))
+    del P
+    Pr = oracle.group_partials(q[rows], inp.qw, wl.fmt)
+    assert np.array_equal(Ps, Pr)
+    assert_rows_close(ys, oracle.epilogue(Pr, s[rows], wl.fmt, inp.gscale, inp.rscale))
+    y2, _ = call(qd, sd, w)                                 # the benchmark's launch
+    assert np.array_equal(host(y2.index_select(0, rows_t)), ys)

@@ -158,6 +158,28 @@ int rad_w8a8_gemv(const int8_t *q, const float *scale, const rad_w8a8_weight *w,
 int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
                   int64_t M, int32_t *partials, rad_stream_t stream);
 
+/*
+ * rad_w8a8_linear -- the whole layer on f32 activations (model card, table
+ * rows "Weights" and "Activations"): rotate and quantise x exactly as
+ * rad_quant_act_i8 with rotate = 1, then contract exactly as rad_w8a8_gemv
+ * (M <= RAD_GEMV_MAX_M) or rad_w8a8_gemm (larger M).  The activation codes
+ * and scales are written out as well as y, and all three equal, bit for bit,
+ * what the separate calls produce.
+ *
+ *   x      f32 [M][K], 16-byte aligned, K <= RAD_QUANT_MAX_K.
+ *   q      int8 [M][K] output, 16-byte aligned.
+ *   scale  f32 [M] output, 4-byte aligned.
+ *   w, y   as for rad_w8a8_gemv.
+ *
+ * For a single token (M == 1, K <= 20480) the three steps run as one kernel:
+ * each workgroup rotates and quantises the token itself while its first
+ * weight rows are already in flight, so no separate quantisation launch
+ * stands in front of the weight stream.  Errors as for the separate calls;
+ * q, scale and y may not overlap each other or any input (RAD_E_ALIAS).
+ */
+int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weight *w, float *y,
+                    int64_t M, rad_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rad_strerror(int status);
 

@@ -31,7 +31,8 @@ GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128}
 RAD_QUANT_MAX_K = 65536
 RAD_GEMV_MAX_M = 128
 
-EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_strerror")
+EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
+           "rad_strerror")
 
 
 class RadError(RuntimeError):
@@ -67,7 +68,9 @@ def lib() -> ctypes.CDLL:
         L.rad_quant_act_i8.argtypes = [vp, vp, vp, i64, i64, ci, vp]
         L.rad_w8a8_gemv.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
         L.rad_w8a8_gemm.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
-        for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm):
+        L.rad_w8a8_linear.argtypes = [vp, vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp]
+        for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm,
+                  L.rad_w8a8_linear):
             f.restype = ci
         L.rad_strerror.argtypes = [ci]
         L.rad_strerror.restype = ctypes.c_char_p
@@ -203,11 +206,23 @@ def w8a8_gemm(q, scale, w: W8A8Weight, y=None, partials=None):
     return _linear_call(lib().rad_w8a8_gemm, "rad_w8a8_gemm", q, scale, w, y, partials)
 
 
-def linear(x, w: W8A8Weight):
-    """The whole layer on f32 activations: rotate + quantise, then contract."""
-    q, s = quant_act_i8(x, rotate=True)
-    if q.shape[0] <= RAD_GEMV_MAX_M:
-        y, _ = w8a8_gemv(q, s, w)
-    else:
-        y, _ = w8a8_gemm(q, s, w)
-    return y
+def linear(x, w: W8A8Weight, q=None, scale=None, y=None):
+    """The whole layer on f32 ``x`` [M][K]: returns (y, q, scale)."""
+    torch = _torch()
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    if K != w.K:
+        raise ValueError("x has K=%d, weight has K=%d" % (K, w.K))
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    _dev(y, torch.float32, "y")
+    d = w.desc()
+    _check(lib().rad_w8a8_linear(x.data_ptr(), q.data_ptr(), scale.data_ptr(), ctypes.byref(d),
+                                 y.data_ptr(), M, _stream(x)), "rad_w8a8_linear")
+    return y, q, scale

@@ -8,18 +8,22 @@
 // then y = s_m * (r_n) * 2^-7 * sum_g scale[n][g] * P[m][n][g].
 //
 // Two kernels:
-//   gemv_m1_kernel   M == 1.  Each wave streams whole weight rows with fully
-//                    coalesced 16-byte loads (a wave reads 1 KiB contiguous per
-//                    load instruction) and v_dot4 against activation codes held
-//                    in registers.  For the u8 format the epilogue is exact
-//                    integer arithmetic up to one f64 product, rounded once.
+//   decode_kernel    M == 1.  Waves stream weight rows four at a time with
+//                    coalesced 16-byte loads and v_dot4 against activation
+//                    codes held in registers; optionally fused with the
+//                    rotation and quantisation of the token.  For the u8 format
+//                    the epilogue is exact integer arithmetic up to one f64
+//                    product, rounded once.
 //   skinny_kernel    2 <= M <= 128.  Each wave owns 16 weight rows and streams
 //                    them straight from HBM into the B operand of
 //                    v_mfma_i32_16x16x64_i8; the activation codes of all M
 //                    tokens are staged per K group in LDS and shared by the
 //                    workgroup's 4 waves.
+#include <algorithm>
+
 #include "rad_device.h"
 #include "rad_launch.h"
+#include "rotate_quant.h"
 
 namespace rad {
 namespace {
@@ -28,145 +32,303 @@ constexpr int kFmtU8 = 0;
 constexpr int kFmtHead = 1;
 
 // ------------------------------------------------------------- M == 1 ----
-// Lane l of a wave handles 16-byte chunks c = l + 64 t (t < CPL) of every row;
-// chunk c lies in group c / (GW/16).  U rows are in flight per buffer and two
-// buffers alternate, so 2*U*CPL 16-byte loads per lane can be outstanding.
-template <int FMT, int CPL, int U, bool WRITE_P>
-__global__ __launch_bounds__(256) void gemv_m1_kernel(const int8_t *__restrict__ q,
-                                                      const float *__restrict__ scale,
-                                                      const int8_t *__restrict__ codes,
-                                                      const void *__restrict__ gscale,
-                                                      const uint16_t *__restrict__ rscale,
-                                                      float *__restrict__ y,
-                                                      int32_t *__restrict__ partials, int N, int K,
-                                                      int rpw) {
-    constexpr int GW16 = (FMT == kFmtU8) ? 16 : 8;   // chunks per group
+// Layout: a wave streams 4 weight rows at a time (a "quad"), one 16-lane DPP
+// row per weight row.  In step t, lane l16 of a DPP row reads the 16 bytes
+// c = l16 + 16 t of its weight row, so one load instruction of the wave reads
+// 4 x 256 contiguous bytes and, for the u8 format, step t is exactly group t.
+// A quad's cross-lane reduction is 4 DPP butterflies inside each 16-lane row,
+// shared by the 4 rows.  Quads are dealt to waves round-robin (wave w takes
+// quads w, w + W, ...), so at any moment the whole GPU streams one contiguous
+// window of the weight matrix.  A ring of D 16-byte loads per lane is kept in
+// flight across quad boundaries; the quad's steps are padded to SP, a multiple
+// of D, with empty steps.  The wave's group and row scales are staged in LDS
+// once, so no scale load sits in the in-order vector-memory queue.
+//
+// u8 format: every partial and every u8-scaled sum is exact integer
+// arithmetic; S = sum_g u8[n][g] P[n][g] is formed exactly and
+// y = s * r * 2^-7 * S is evaluated in f64 in that order and rounded once, so
+// this path reproduces the oracle's output bit for bit.
+//
+// FUSED: the workgroup first rotates and quantises the f32 token itself (the
+// same device code and bits as rad_quant_act_i8) while its first weight loads
+// are in flight; block 0 also writes the codes and the scale out.
+constexpr int kScBytes = 2048;   // per-wave LDS staging of group scales
+constexpr int kRsBytes = 128;    // per-wave LDS staging of row scales (16 quads)
+constexpr int kM1MaxK = 20480;   // K handled by the one-token path
+
+template <int FMT, int STEPS, int D, bool WRITE_P, bool FUSED>
+__global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x,
+                                                     int8_t *__restrict__ qio,
+                                                     float *__restrict__ sio,
+                                                     const int8_t *__restrict__ codes,
+                                                     const void *__restrict__ gscale,
+                                                     const uint16_t *__restrict__ rscale,
+                                                     float *__restrict__ y,
+                                                     int32_t *__restrict__ partials, int N, int K) {
+    constexpr int GW16 = (FMT == kFmtU8) ? 16 : 8;    // 16-byte chunks per group
+    constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;      // bytes per group scale
+    constexpr int SP = ((STEPS + D - 1) / D) * D;     // steps per quad incl. padding
+    constexpr int NQ = (STEPS + 7) / 8;               // 16-block rotation steps (K <= 256 STEPS)
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[4][kScBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rs_lds[4][kRsBytes];
+    __shared__ __attribute__((aligned(16))) int8_t q_lds[STEPS * 256];
+    __shared__ float red[4];
+
     const int lane = threadIdx.x & 63;
-    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int n_begin = wave * rpw;
-    if (n_begin >= N) return;
-    const int n_end = min(n_begin + rpw, N);
+    const int wid = threadIdx.x >> 6;
+    const int l16 = lane & 15;
+    const int r4 = lane >> 4;                          // weight row inside the quad
+    const int wave = blockIdx.x * 4 + wid;
+    const int W = gridDim.x * 4;
+    const int nq = (N + 3) >> 2;
+    const int cnt = wave < nq ? (nq - wave + W - 1) / W : 0;   // quads of this wave
     const int nchunk = K >> 4;
     const int G = nchunk / GW16;
+    const int qsb = 4 * G * ESZ;                       // scale bytes of one quad (multiple of 4)
+    const int64_t allsb = static_cast<int64_t>(N) * G * ESZ;
 
-    v4i a[CPL];
-#pragma unroll
-    for (int t = 0; t < CPL; ++t) {
-        const int c = lane + 64 * t;
-        a[t] = (c < nchunk) ? ld16(q + 16 * c) : v4i{0, 0, 0, 0};
+    // 1. this wave's group and row scales, straight into LDS, dword by dword.
+    //    A dword that would run past the end of an array is loaded bytewise.
+    {
+        const uint8_t *gs = static_cast<const uint8_t *>(gscale);
+        const int nd = cnt * qsb / 4;
+        for (int j0 = 0; j0 < nd; j0 += 64) {
+            const int j = j0 + lane;
+            const int qi = (4 * j) / qsb;
+            const int64_t src = static_cast<int64_t>(4 * (wave + qi * W)) * G * ESZ + (4 * j - qi * qsb);
+            const bool ok = j < nd;
+            if (ok && src + 4 <= allsb) {
+                g2lds_dword(gs + src, &sc_lds[wid][4 * j0]);
+            } else if (ok && src < allsb) {
+                for (int b = 0; b < 4 && src + b < allsb; ++b) sc_lds[wid][4 * j + b] = gs[src + b];
+            }
+        }
+        if constexpr (FMT == kFmtU8) {
+            const uint8_t *rs = reinterpret_cast<const uint8_t *>(rscale);
+            const int j = lane;                        // 2 dwords per quad, <= 16 quads
+            const int qi = j >> 1;
+            const int64_t src = static_cast<int64_t>(8) * (wave + qi * W) + 4 * (j & 1);
+            const bool ok = j < 2 * cnt;
+            if (ok && src + 4 <= 2 * static_cast<int64_t>(N)) {
+                g2lds_dword(rs + src, &rs_lds[wid][0]);
+            } else if (ok && src < 2 * static_cast<int64_t>(N)) {
+                for (int b = 0; b < 4 && src + b < 2 * static_cast<int64_t>(N); ++b) rs_lds[wid][4 * j + b] = rs[src + b];
+            }
+        }
     }
-    const float s = scale[0];
 
-    auto load_rows = [&](v4i (&w)[U][CPL], int n) {
+    // 2. the token: f32 into registers (fused) or its codes straight into LDS
+    Blk8 xv[FUSED ? NQ : 1];
+    float s = 0.0f;
+    const int nblk = K >> 7;
+    if constexpr (FUSED) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int nn = n + u;
-            const int8_t *row = codes + static_cast<int64_t>(nn) * K;
-#pragma unroll
-            for (int t = 0; t < CPL; ++t) {
-                const int c = lane + 64 * t;
-                w[u][t] = (nn < n_end && c < nchunk) ? ld16(row + 16 * c) : v4i{0, 0, 0, 0};
-            }
-        }
-    };
-
-    auto finish_rows = [&](const v4i (&w)[U][CPL], int n) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int nn = n + u;
-            if (nn >= n_end) break;                       // wave-uniform
-            if constexpr (FMT == kFmtU8) {
-                const uint8_t *g8 = static_cast<const uint8_t *>(gscale) + static_cast<int64_t>(nn) * G;
-                int acc = 0;                              // |acc| <= CPL * 258064 * 255 < 2^31
-#pragma unroll
-                for (int t = 0; t < CPL; ++t) {
-                    const int c = lane + 64 * t;
-                    if (c < nchunk) {
-                        const int p = dot16_i8(w[u][t], a[t], 0);
-                        const int g = c / GW16;
-                        acc += p * static_cast<int>(g8[g]);
-                        if constexpr (WRITE_P) {
-                            const int pg = row16_sum(p);
-                            if ((lane & 15) == 0) partials[static_cast<int64_t>(nn) * G + g] = pg;
-                        }
-                    }
-                }
-                // exact 64-lane sum: split into 16-bit halves that cannot overflow
-                const int hi = wave_sum_i32(acc >> 16);
-                const int lo = wave_sum_i32(acc & 0xFFFF);
-                if (lane == 0) {
-                    const int64_t S = static_cast<int64_t>(hi) * 65536 + lo;
-                    const double r = static_cast<double>(bf16_to_f32(rscale[nn]));
-                    y[nn] = static_cast<float>(static_cast<double>(s) * r * 0x1p-7 * static_cast<double>(S));
-                }
+        for (int it = 0; it < NQ; ++it) {
+            const int blk = (it * 4 + wid) * 4 + r4;
+            if (blk < nblk) {
+                const float *p = x + blk * 128 + 4 * l16;
+                xv[it].lo = *reinterpret_cast<const float4 *>(p);
+                xv[it].hi = *reinterpret_cast<const float4 *>(p + 64);
             } else {
-                const uint16_t *gb = static_cast<const uint16_t *>(gscale) + static_cast<int64_t>(nn) * G;
-                float acc = 0.0f;
-#pragma unroll
-                for (int t = 0; t < CPL; ++t) {
-                    const int c = lane + 64 * t;
-                    if (c < nchunk) {
-                        const int p = dot16_i8(w[u][t], a[t], 0);
-                        const int g = c / GW16;
-                        acc += static_cast<float>(p) * bf16_to_f32(gb[g]);
-                        if constexpr (WRITE_P) {
-                            const int pg = row8_sum(p);
-                            if ((lane & 7) == 0) partials[static_cast<int64_t>(nn) * G + g] = pg;
-                        }
-                    }
-                }
-                const float tot = wave_sum_f32(acc);
-                if (lane == 0) y[nn] = (s * 0x1p-7f) * tot;
+                xv[it].lo = make_float4(0.f, 0.f, 0.f, 0.f);
+                xv[it].hi = xv[it].lo;
             }
         }
-    };
+    } else {
+        for (int d0 = wid * 64; d0 < K / 4; d0 += 256) {
+            if (d0 + lane < K / 4)
+                g2lds_dword(qio + 4 * (d0 + lane), &q_lds[4 * d0]);
+        }
+        s = sio[0];
+    }
 
-    v4i w0[U][CPL], w1[U][CPL];
-    load_rows(w0, n_begin);
-    for (int n = n_begin; n < n_end; n += 2 * U) {
-        if (n + U < n_end) load_rows(w1, n + U);
-        finish_rows(w0, n);
-        if (n + U >= n_end) break;
-        if (n + 2 * U < n_end) load_rows(w0, n + 2 * U);
-        finish_rows(w1, n + U);
+    // 3. the first D weight loads of the ring.  Loads are branch-free: a quad
+    //    past the wave's last one, or a row past N, is clamped to an in-bounds
+    //    row (a re-read of cached data) whose result is never stored; STEPS is
+    //    exactly ceil(K / 256), so only the last step can hold lanes past the
+    //    end of a row (head format), and those are clamped and not accumulated.
+    auto row_ptr = [&](int i) -> const int8_t * {
+        const int ii = min(i, cnt - 1);
+        const int row = min(4 * (wave + ii * W) + r4, N - 1);
+        return codes + static_cast<int64_t>(row) * K + 16 * l16;
+    };
+    auto wload = [&](const int8_t *rp, int t) -> v4i {
+        if (t >= STEPS) return v4i{0, 0, 0, 0};       // padding step: no load
+        if (t == STEPS - 1) {
+            const int c = min(l16 + 16 * t, nchunk - 1);
+            return ld16(rp - 16 * l16 + 16 * c);
+        }
+        return ld16(rp + 256 * t);
+    };
+    v4i ring[D];
+    const int8_t *rp_next = row_ptr(0);
+    if (cnt > 0) {
+#pragma unroll
+        for (int t = 0; t < D; ++t) ring[t] = wload(rp_next, t);
+    }
+
+    // 4. fused: rotate and quantise the token into LDS (and, block 0, to q / s)
+    if constexpr (FUSED) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            fwht128_regs(xv[it], l16);
+            amax = fmaxf(amax, fmaxf(amax4(xv[it].lo), amax4(xv[it].hi)));
+        }
+        amax = wave_max_f32(amax);
+        if (lane == 0) red[wid] = amax;
+        __syncthreads();
+        s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / 127.0f;
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            const int blk = (it * 4 + wid) * 4 + r4;
+            if (blk < nblk) {
+                uint32_t lo = 0, hi = 0;
+                if (s != 0.0f) {
+                    lo = pack4(xv[it].lo, s);
+                    hi = pack4(xv[it].hi, s);
+                }
+                const int off = blk * 128 + 4 * l16;
+                *reinterpret_cast<uint32_t *>(&q_lds[off]) = lo;
+                *reinterpret_cast<uint32_t *>(&q_lds[off + 64]) = hi;
+                if (blockIdx.x == 0) {
+                    *reinterpret_cast<uint32_t *>(qio + off) = lo;
+                    *reinterpret_cast<uint32_t *>(qio + off + 64) = hi;
+                }
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x == 0) sio[0] = s;
+    }
+    // every LDS transfer above has landed (this also waits for the ring,
+    // whose first entry the loop needs at once), then make it workgroup-visible
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // 5. the weight stream
+    for (int i = 0; i < cnt; ++i) {
+        const int row = 4 * (wave + i * W) + r4;
+        const int8_t *rp_cur = rp_next;
+        rp_next = row_ptr(i + 1);
+        const uint8_t *scq = &sc_lds[wid][i * qsb + r4 * G * ESZ];
+        // an offset the compiler cannot see through keeps the activation reads
+        // inside the loop (re-read from LDS each quad) instead of holding all
+        // STEPS chunks in registers
+        int qoff = 0;
+        asm volatile("" : "+v"(qoff));
+        int acc = 0, acc_hi = 0;                       // u8: exact integer sums
+        float accf = 0.0f;                             // head: f32
+#pragma unroll
+        for (int t = 0; t < SP; ++t) {
+            if (t < STEPS) {
+                const int c = l16 + 16 * t;
+                const v4i av = *reinterpret_cast<const v4i *>(&q_lds[16 * c + qoff]);
+                const int p = dot16_i8(ring[t % D], av, 0);
+                if constexpr (FMT == kFmtU8) {
+                    const int prod = p * static_cast<int>(scq[t]);     // |prod| < 2^26
+                    if constexpr (STEPS <= 32) {
+                        acc += prod;                                   // < 32 * 2^26
+                    } else {
+                        acc += prod & 0xFFFF;
+                        acc_hi += prod >> 16;
+                    }
+                    if constexpr (WRITE_P) {
+                        const int pg = row16_sum(p);
+                        if (l16 == 0 && row < N) partials[static_cast<int64_t>(row) * G + t] = pg;
+                    }
+                } else if (c < nchunk) {
+                    const int g = 2 * t + (l16 >> 3);
+                    const uint16_t b = *reinterpret_cast<const uint16_t *>(&scq[2 * g]);
+                    accf += static_cast<float>(p) * bf16_to_f32(b);
+                    if constexpr (WRITE_P) {
+                        const int pg = row8_sum(p);
+                        if ((l16 & 7) == 0 && row < N) partials[static_cast<int64_t>(row) * G + g] = pg;
+                    }
+                }
+            }
+            ring[t % D] = (t + D < SP) ? wload(rp_cur, t + D) : wload(rp_next, t + D - SP);
+            // keep the steps in order: without this the scheduler hoists every
+            // step's LDS read to the top of the quad and holds them all
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (FMT == kFmtU8) {
+            // exact 16-lane sums of the 16-bit halves; S = hi * 2^16 + lo
+            int hi, lo;
+            if constexpr (STEPS <= 32) {
+                hi = row16_sum(acc >> 16);
+                lo = row16_sum(acc & 0xFFFF);
+            } else {
+                hi = row16_sum(acc_hi + (acc >> 16));
+                lo = row16_sum(acc & 0xFFFF);
+            }
+            if (l16 == 0 && row < N) {
+                const int64_t S = static_cast<int64_t>(hi) * 65536 + lo;
+                const uint16_t rb = *reinterpret_cast<const uint16_t *>(&rs_lds[wid][8 * i + 2 * r4]);
+                const double rn = static_cast<double>(bf16_to_f32(rb));
+                y[row] = static_cast<float>(static_cast<double>(s) * rn * 0x1p-7 * static_cast<double>(S));
+            }
+        } else {
+            accf += lane_xor<1>(accf);
+            accf += lane_xor<2>(accf);
+            accf += lane_xor<4>(accf);
+            accf += lane_xor<8>(accf);
+            if (l16 == 0 && row < N) y[row] = (s * 0x1p-7f) * accf;
+        }
     }
 }
 
-template <int FMT, int CPL>
-hipError_t launch_m1_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int32_t *P,
-                       hipStream_t st) {
-    constexpr int U = (CPL <= 4) ? 4 : (CPL <= 8 ? 2 : 1);
+// Quads per wave: about TARGET waves in all, bounded by the LDS staging.
+inline int decode_quads_per_wave(int64_t N, int64_t K, int fmt, int target_waves) {
+    const int G = static_cast<int>(K / (fmt == kFmtU8 ? 256 : 128));
+    const int esz = fmt == kFmtU8 ? 1 : 2;
+    const int nq = static_cast<int>((N + 3) / 4);
+    int qpw = (nq + target_waves - 1) / target_waves;
+    qpw = std::min(qpw, kScBytes / (4 * G * esz));
+    qpw = std::min(qpw, kRsBytes / 8);
+    return std::max(qpw, 1);
+}
+
+
+template <int FMT, int STEPS, bool FUSED>
+hipError_t launch_m1_t(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
+                       int32_t *P, hipStream_t st) {
+    // ring depth: a divisor of STEPS near 10 when there is one, else pad to 8s
+    constexpr int D = (STEPS <= 12) ? STEPS
+                    : (STEPS % 10 == 0) ? 10 : (STEPS % 12 == 0) ? 12 : (STEPS % 9 == 0) ? 9
+                    : (STEPS % 11 == 0) ? 11 : (STEPS % 8 == 0) ? 8 : 8;
     const int N = static_cast<int>(w.N);
-    // Aim for 8 waves per CU on 256 CUs, equal rows per wave.
-    const int target_waves = 256 * 8;
-    int rpw = (N + target_waves - 1) / target_waves;
-    if (rpw < 1) rpw = 1;
-    const int waves = (N + rpw - 1) / rpw;
+    const int nq = (N + 3) / 4;
+    const int qpw = decode_quads_per_wave(w.N, w.K, FMT, 3072);   // ~12 waves per CU
+    const int waves = (nq + qpw - 1) / qpw;
     const int grid = (waves + 3) / 4;
-    auto kern = P ? gemv_m1_kernel<FMT, CPL, U, true> : gemv_m1_kernel<FMT, CPL, U, false>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, q, s, w.codes, w.gscale, w.rscale, y, P,
-                       N, static_cast<int>(w.K), rpw);
+    auto kern = P ? decode_kernel<FMT, STEPS, D, true, FUSED> : decode_kernel<FMT, STEPS, D, false, FUSED>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, x, q, s, w.codes, w.gscale, w.rscale, y, P,
+                       N, static_cast<int>(w.K));
     return hipGetLastError();
 }
 
-template <int FMT>
-hipError_t launch_m1(const int8_t *q, const float *s, const WeightArgs &w, float *y, int32_t *P,
+// Step counts (ceil(K / 256)) with a one-token kernel; other K use the MFMA path.
+#define RAD_M1_STEPS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(14) \
+    X(16) X(20) X(24) X(28) X(32) X(40) X(48) X(56) X(64) X(68) X(72) X(80)
+
+inline bool m1_steps_supported(int64_t K) {
+    const int steps = static_cast<int>((K + 255) / 256);
+    switch (steps) {
+#define RAD_M1_YES(S) case S: return true;
+        RAD_M1_STEPS(RAD_M1_YES)
+#undef RAD_M1_YES
+        default: return false;
+    }
+}
+
+template <int FMT, bool FUSED>
+hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y, int32_t *P,
                      hipStream_t st) {
-    const int cpl = static_cast<int>((w.K / 16 + 63) / 64);
-    switch (cpl) {
-        case 1: return launch_m1_t<FMT, 1>(q, s, w, y, P, st);
-        case 2: return launch_m1_t<FMT, 2>(q, s, w, y, P, st);
-        case 3: return launch_m1_t<FMT, 3>(q, s, w, y, P, st);
-        case 4: return launch_m1_t<FMT, 4>(q, s, w, y, P, st);
-        case 5: return launch_m1_t<FMT, 5>(q, s, w, y, P, st);
-        case 6: return launch_m1_t<FMT, 6>(q, s, w, y, P, st);
-        case 7: case 8: return launch_m1_t<FMT, 8>(q, s, w, y, P, st);
-        case 9: case 10: case 11: case 12: return launch_m1_t<FMT, 12>(q, s, w, y, P, st);
-        case 13: case 14: case 15: case 16: return launch_m1_t<FMT, 16>(q, s, w, y, P, st);
-        case 17: return launch_m1_t<FMT, 17>(q, s, w, y, P, st);
-        case 18: case 19: case 20: case 21: case 22: case 23: case 24:
-            return launch_m1_t<FMT, 24>(q, s, w, y, P, st);
-        default: return launch_m1_t<FMT, 32>(q, s, w, y, P, st);
+    const int steps = static_cast<int>((w.K + 255) / 256);
+    switch (steps) {
+#define RAD_M1_CASE(S) case S: return launch_m1_t<FMT, S, FUSED>(x, q, s, w, y, P, st);
+        RAD_M1_STEPS(RAD_M1_CASE)
+#undef RAD_M1_CASE
+        default: return hipErrorInvalidValue;           // excluded by m1_supported
     }
 }
 
@@ -336,16 +498,32 @@ hipError_t launch_skinny(const int8_t *q, const float *s, const WeightArgs &w, f
     }
 }
 
+inline bool m1_supported(int64_t K, int fmt) {
+    const int G = static_cast<int>(K / (fmt == kFmtU8 ? 256 : 128));
+    const int esz = fmt == kFmtU8 ? 1 : 2;
+    return K <= kM1MaxK && 4 * G * esz <= kScBytes && m1_steps_supported(K);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st) {
-    if (M == 1 && w.K <= 32768) {
-        return w.fmt == kFmtU8 ? launch_m1<kFmtU8>(q, s, w, y, partials, st)
-                               : launch_m1<kFmtHead>(q, s, w, y, partials, st);
+    if (M == 1 && m1_supported(w.K, w.fmt)) {
+        int8_t *qi = const_cast<int8_t *>(q);            // read only: FUSED == false
+        float *si = const_cast<float *>(s);
+        return w.fmt == kFmtU8 ? launch_m1<kFmtU8, false>(nullptr, qi, si, w, y, partials, st)
+                               : launch_m1<kFmtHead, false>(nullptr, qi, si, w, y, partials, st);
     }
     return w.fmt == kFmtU8 ? launch_skinny<kFmtU8>(q, s, w, y, M, partials, st)
                            : launch_skinny<kFmtHead>(q, s, w, y, M, partials, st);
+}
+
+bool fused_decode_supported(const WeightArgs &w, int64_t M) { return M == 1 && m1_supported(w.K, w.fmt); }
+
+hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
+                               hipStream_t st) {
+    return w.fmt == kFmtU8 ? launch_m1<kFmtU8, true>(x, q, s, w, y, nullptr, st)
+                           : launch_m1<kFmtHead, true>(x, q, s, w, y, nullptr, st);
 }
 
 }  // namespace rad

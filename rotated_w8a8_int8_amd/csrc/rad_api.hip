@@ -108,6 +108,34 @@ int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w,
                                        static_cast<hipStream_t>(stream)));
 }
 
+int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weight *w, float *y,
+                    int64_t M, rad_stream_t stream) {
+    int rc = check_linear(q, scale, w, y, M, nullptr, kI32Max);
+    if (rc < 0) return rc;
+    if (w->K > RAD_QUANT_MAX_K) return RAD_E_RANGE;
+    if (rc > 0) return RAD_OK;                       // empty
+    if (!x) return RAD_E_NULL;
+    if (!aligned(x, 16)) return RAD_E_ALIGN;
+    const int64_t N = w->N, K = w->K;
+    const int gw = group_width(w->fmt);
+    const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
+    const Span xs = span(x, M * K * 4), qs = span(q, M * K), ss = span(scale, M * 4),
+               ys = span(y, M * N * 4);
+    const Span ws[] = {span(w->codes, N * K), span(w->gscale, N * (K / gw) * esz),
+                       w->rscale ? span(w->rscale, N * 2) : Span{0, 0}};
+    if (overlap(xs, qs) || overlap(xs, ss) || overlap(qs, ss) || overlap(xs, ys)) return RAD_E_ALIAS;
+    for (const Span &o : ws)
+        if (overlap(qs, o) || overlap(ss, o)) return RAD_E_ALIAS;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const rad::WeightArgs wa = weight_args(w);
+    if (rad::fused_decode_supported(wa, M)) return hip_status(rad::launch_fused_decode(x, q, scale, wa, y, st));
+    hipError_t e = rad::launch_quant_act(x, q, scale, M, K, 1, st);
+    if (e != hipSuccess) return RAD_E_HIP;
+    e = (M <= RAD_GEMV_MAX_M) ? rad::launch_gemv(q, scale, wa, y, M, nullptr, st)
+                              : rad::launch_gemm(q, scale, wa, y, M, nullptr, st);
+    return hip_status(e);
+}
+
 const char *rad_strerror(int status) {
     switch (status) {
         case RAD_OK: return "success";

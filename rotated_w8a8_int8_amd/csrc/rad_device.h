@@ -11,6 +11,16 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Global -> LDS dword copy without a register round trip: every active lane
+// copies the 4 bytes at its own `src` to `lds_base + 4 * lane`; `lds_base`
+// must be the same for the whole wave.  Completion is tracked by the vector
+// memory counter, like any load: wait on it before reading the LDS words.
+typedef __attribute__((address_space(1))) const void gptr_t;
+typedef __attribute__((address_space(3))) void lptr_t;
+__device__ __forceinline__ void g2lds_dword(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_base, 4, 0, 0);
+}
+
 // bf16 bit pattern -> f32 (a bf16 is the high half of an f32; exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -129,3 +129,22 @@ def test_linear_validation(name, max_m):
     assert call(desc(), y=C + 4096) == B.RAD_E_ALIAS                # y over codes
     assert call(desc(), p=D) == B.RAD_E_ALIAS                       # partials over gscale
     assert call(desc(), p=F + 64) == B.RAD_E_ALIAS                  # partials over y
+
+
+def test_linear_entry_validation():
+    f = B.lib().rad_w8a8_linear
+
+    def call(d, M=4, x=Bp + 0x100000, q=A, s=Bp, y=F):
+        return f(x, q, s, None if d is None else ctypes.byref(d), y, M, None)
+
+    assert call(None) == B.RAD_E_NULL
+    assert call(desc(fmt=9)) == B.RAD_E_FMT
+    assert call(desc(K=384)) == B.RAD_E_SHAPE
+    assert call(desc(K=B.RAD_QUANT_MAX_K + 256)) == B.RAD_E_RANGE
+    assert call(desc(), M=0, x=0, q=0, s=0, y=0) == B.RAD_OK
+    assert call(desc(), x=0) == B.RAD_E_NULL
+    assert call(desc(), q=0) == B.RAD_E_NULL
+    assert call(desc(), x=Bp + 0x100000 + 4) == B.RAD_E_ALIGN
+    assert call(desc(), q=Bp + 0x100000 + 64) == B.RAD_E_ALIAS      # codes out over x
+    assert call(desc(), s=D) == B.RAD_E_ALIAS                       # scales out over gscale
+    assert call(desc(), y=Bp + 0x100000) == B.RAD_E_ALIAS           # y over x

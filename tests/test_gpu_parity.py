@@ -216,6 +216,35 @@ def test_repeatable(torch):
         assert np.array_equal(host(y2), y1) and np.array_equal(host(P2), P1)
 
 
+# ------------------------------------------------------------ whole layer --
+
+@pytest.mark.parametrize("M,K,N,fmt", [
+    (1, 5120, 34816, 0), (1, 128, 5, 1), (1, 256, 300, 0), (1, 640, 1000, 1), (1, 17408, 333, 0),
+    (1, 20480, 64, 0), (1, 20736, 64, 0), (4, 512, 256, 0), (64, 1024, 100, 1), (200, 512, 96, 0),
+])
+def test_linear_whole_layer(torch, M, K, N, fmt):
+    """rad_w8a8_linear (fused for one token) equals the separate calls bit for bit."""
+    inp = W.make(M, K, N, fmt, seed=K + N)
+    w = weight(torch, inp)
+    xd = dev(torch, inp.x)
+    y, q, s = B.linear(xd, w)
+    qr, sr = oracle.quant_act_i8(inp.x)
+    assert np.array_equal(host(q), qr)
+    assert np.array_equal(host(s).view(np.int32), sr.view(np.int32))
+    q2, s2 = B.quant_act_i8(xd)
+    call = B.w8a8_gemv if M <= B.RAD_GEMV_MAX_M else B.w8a8_gemm
+    y2, _ = call(q2, s2, w)
+    assert np.array_equal(host(y).view(np.int32), host(y2).view(np.int32))
+    assert_rows_close(host(y), oracle.linear(qr, sr, inp.qw, fmt, inp.gscale, inp.rscale))
+
+
+def test_linear_zero_token(torch):
+    inp = W.make(1, 1024, 70, 0, seed=1)
+    w = weight(torch, inp)
+    y, q, s = B.linear(torch.zeros((1, 1024), dtype=torch.float32, device="cuda"), w)
+    assert host(s)[0] == 0 and not host(q).any() and not host(y).any()
+
+
 # ------------------------------------------------------ full-size workloads --
 
 def sample_rows(M, n, seed):

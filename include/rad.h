@@ -74,8 +74,9 @@ enum rad_format {
  * A quantised weight in the rotated domain.  Codes are int8 in -127..127 and
  * each contiguous 128 of a row's K has already been rotated by H (the
  * 128x128 Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i&j), no
- * normalisation).  codes must be 16-byte aligned.  gscale and rscale have no
- * alignment requirement.
+ * normalisation).  codes must be 16-byte aligned; gscale and rscale must be
+ * 4-byte aligned (the kernels read scales a 32-bit word at a time, never past
+ * the end of either array).
  */
 typedef struct rad_w8a8_weight {
     const int8_t *codes;     /* int8 [N][K]                                   */

@@ -44,7 +44,8 @@ int check_linear(const int8_t *q, const float *scale, const rad_w8a8_weight *w, 
     if (M > max_m || w->N > kI32Max || w->K > kI32Max) return RAD_E_RANGE;
     if (M == 0 || w->N == 0) return 1;  // nothing to do
     if (!q || !scale || !y || !w->codes || !w->gscale) return RAD_E_NULL;
-    if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(scale, 4) || !aligned(y, 4) ||
+    if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(w->gscale, 4) ||
+        (w->rscale && !aligned(w->rscale, 4)) || !aligned(scale, 4) || !aligned(y, 4) ||
         (partials && !aligned(partials, 4)))
         return RAD_E_ALIGN;
     const int64_t N = w->N, K = w->K, G = K / gw;

@@ -20,6 +20,10 @@ typedef __attribute__((address_space(3))) void lptr_t;
 __device__ __forceinline__ void g2lds_dword(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_base, 4, 0, 0);
 }
+// The same with 16 bytes per lane: lane l's 16 bytes land at lds_base + 16 l.
+__device__ __forceinline__ void g2lds_16(const void *src, void *lds_base) {
+    __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_base, 16, 0, 0);
+}
 
 // bf16 bit pattern -> f32 (a bf16 is the high half of an f32; exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -113,6 +117,30 @@ __device__ __forceinline__ int dot16_i8(v4i a, v4i b, int acc) {
     acc = __builtin_amdgcn_sdot4(a.z, b.z, acc, false);
     acc = __builtin_amdgcn_sdot4(a.w, b.w, acc, false);
     return acc;
+}
+
+// Four 16-byte LDS reads issued together and completed before the block
+// ends (the wait is inside the same asm block, so no output register is ever
+// live while its load is still in flight).  Used where LDS is filled by
+// direct global -> LDS loads: the compiler cannot tell such a read from one
+// that aliases a pending direct load and would otherwise drain every
+// outstanding global load before it; the caller's own vmcnt wait and barrier
+// order these reads instead.  Addresses are LDS byte offsets.
+__device__ __forceinline__ void lds_read4_b128(v4i &r0, v4i &r1, v4i &r2, v4i &r3, uint32_t a0,
+                                               uint32_t a1, uint32_t a2, uint32_t a3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+// LDS byte offset of a __shared__ object (the low half of its flat address).
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 // Loads that bypass nothing: plain 16-byte global loads.

@@ -123,6 +123,8 @@ def test_linear_validation(name, max_m):
     assert call(desc(gscale=0)) == B.RAD_E_NULL
     assert call(desc(), q=A + 4) == B.RAD_E_ALIGN
     assert call(desc(codes=C + 8)) == B.RAD_E_ALIGN
+    assert call(desc(gscale=D + 2)) == B.RAD_E_ALIGN
+    assert call(desc(rscale=E + 2)) == B.RAD_E_ALIGN
     assert call(desc(), y=F + 2) == B.RAD_E_ALIGN
     assert call(desc(), p=F + 0x100000 + 1) == B.RAD_E_ALIGN
     assert call(desc(), y=A + 16) == B.RAD_E_ALIAS                  # y over q

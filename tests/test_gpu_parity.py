@@ -164,6 +164,8 @@ def test_gemv_m1_u8_output_is_exact(torch):
 GEMM_SMALL = [
     (1, 256, 16, 0), (5, 512, 256, 0), (130, 512, 130, 0), (257, 768, 300, 1), (128, 1024, 128, 0),
     (200, 256, 33, 0), (300, 640, 70, 1), (129, 2048, 257, 0),
+    # scale arrays of 1..4 bytes (the smallest take the M <= 128 path in chunks)
+    (200, 256, 1, 0), (300, 256, 3, 0), (130, 256, 4, 0), (129, 128, 1, 1), (260, 128, 2, 1),
 ]
 
 

@@ -9,19 +9,23 @@
 //
 // Tiling: a 512-thread workgroup owns a 256 x 128 tile of y; its 8 waves
 // (two per SIMD) own 64 x 64 sub-tiles, each a 2 x 2 grid of 32 x 32 MFMA
-// tiles (64 int32 partials + 64 f32 accumulators per lane).  K is walked in
-// 128-byte stages through a ring of 3 LDS buffers (144 KiB) filled by direct
-// global -> LDS 16-byte loads, so two stages are always in flight while a
+// tiles (per lane: 2 x 64 int32 partials, 64 f32 accumulators).  K is walked
+// in 128-byte stages through a ring of 3 LDS buffers (144 KiB) filled by
+// direct global -> LDS 16-byte loads, so two stages are in flight while a
 // third is consumed and no register holds staged data.  Each 128-byte row's
-// eight 16-byte chunks are XOR-permuted by (row / 2) mod 8, so the 16 rows
-// read by one ds_read_b128 phase cover all 64 banks.  A group's fold into F
-// is issued tile by tile right before that tile's first MFMA of the next
-// group, so the VALU work overlaps the matrix cores.
+// eight 16-byte chunks are XOR-permuted (row-dependent), so the rows one
+// ds_read_b128 phase reads cover all banks, while each direct load still
+// reads whole 128-byte row segments with consecutive lanes.  The per-group
+// fold (convert + multiply-add per partial) is VALU work of about half the
+// matrix time: partials are double-buffered by group parity so that a
+// group's fold runs one tile at a time under the next group's matrix ops.
 //
 // Launch order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD is
 // handed a slab of 4 M-tiles x all N-tiles, walked M-fastest, so the ~32
 // workgroups an XCD runs at once share their activation rows and weight
 // columns in that XCD's L2.
+#include <type_traits>
+
 #include "rad_device.h"
 #include "rad_launch.h"
 
@@ -30,7 +34,12 @@ namespace {
 
 constexpr int kFmtU8 = 0;
 constexpr int kBM = 256, kBN = 128, kKC = 128;
-constexpr int kThreads = 512;
+constexpr int kWavesM = 4, kWavesN = 2;        // 8 waves, two per SIMD
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;   // wave tile 64 x 64
+constexpr int kTM = kWTM / 32, kTN = kWTN / 32;             // of 32 x 32 MFMA tiles
+static_assert(kWTN == 64, "one scale dword per lane covers a wave tile's columns");
 constexpr int kGroupM = 4;   // M-tiles per XCD slab
 
 __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm, int &tn) {
@@ -48,18 +57,21 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm
 
 constexpr int kStages = 3;
 constexpr int kABytes = kBM * kKC, kBBytes = kBN * kKC;   // one stage of each operand
-constexpr int kDmaA = kABytes / 1024 / 8;                 // 1 KiB loads per wave per stage
-constexpr int kDmaB = kBBytes / 1024 / 8;
+constexpr int kDmaA = kABytes / 1024 / kWaves;            // 1 KiB loads per wave per stage
+constexpr int kDmaB = kBBytes / 1024 / kWaves;
 constexpr int kDmaPerStage = kDmaA + kDmaB;
 
-// LDS layout of a 128-byte-deep operand stage: row r lives in 1 KiB block
-// r / 8, chunk-major inside the block; logical 16-byte chunk c of row r sits
-// at slot 8 * (c ^ ((r / 8) & 1)) + r % 8.  A ds_read_b128 phase (16 rows,
-// one chunk) then covers all 64 banks, k-step kk of a fragment is a constant
-// 256 * kk away from k-step 0, and one direct-load instruction fills one
-// block: 8 rows x 128 contiguous bytes.
-__device__ __forceinline__ int lds_row_base(int row, int c_lo) {
-    return (row >> 3) * 1024 + 16 * (row & 7) + 128 * (c_lo ^ ((row >> 3) & 1));
+// LDS layout of a 128-byte-deep operand stage: row r occupies bytes
+// 128 r .. 128 r + 127 (one direct-load instruction fills 8 whole rows, 8
+// lanes per row, so each lane quad reads 64 contiguous bytes of one row and
+// the loads coalesce), with its logical 16-byte chunk c stored in slot
+// c ^ swz(r), swz(r) = (r mod 8) ^ ((r / 8) mod 2).  Fragment reads fetch
+// one chunk of consecutive rows: any 8 aligned consecutive rows then hit 8
+// different 16-byte slots of a 128-byte bank line, and any 16 hit all 16
+// slots of a 256-byte line (rows of equal parity differ in the swizzle).
+__device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int lds_chunk_addr(int row, int c) {
+    return 128 * row + 16 * (c ^ lds_swz(row));
 }
 
 template <int FMT, bool WRITE_P>
@@ -77,12 +89,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
     __shared__ __attribute__((aligned(1024))) int8_t Bs[kStages][kBBytes];
     // per group: each wave's 64 columns, one dword each (the dword that holds
     // the column's scale), filled by direct loads like the operands
-    __shared__ __attribute__((aligned(256))) uint32_t Ss[kStages][8][64];
+    __shared__ __attribute__((aligned(256))) uint32_t Ss[kStages][kWaves][kWTN];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
-    const int wm = wid >> 1, wn = wid & 1;            // 4 x 2 waves
+    const int wu = __builtin_amdgcn_readfirstlane(wid);  // the same, known uniform
+    const int wm = wid / kWavesN, wn = wid % kWavesN;
     const int li = lane & 31, lq = lane >> 5;          // MFMA lane: row/col, k half
     int tmi, tni;
     tile_of(blockIdx.x, tiles_m, tiles_n, tmi, tni);
@@ -91,35 +104,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
     const int NK = K / kKC;
 
     // ---- direct global -> LDS loads of one stage.  Wave w fills 1 KiB blocks
-    // (8 rows x 128 B); lane l of a block is row l / 8, physical chunk l % 8,
-    // and fetches the logical chunk that the swizzle puts there.  Rows past
-    // M or N are clamped to the last row (never stored).
-    // lane l of a block's load: row l % 8, physical chunk l / 8.  Sources are
-    // a wave-uniform base (tile origin + k offset) plus a 32-bit lane offset.
-    const int drow = lane & 7, dphys = lane >> 3;
+    // (8 rows x 128 B); lane l of a block's load is row l / 8, physical slot
+    // l % 8, and fetches the logical chunk the swizzle puts in that slot.
+    // Sources are a wave-uniform base (tile origin + k offset) plus a 32-bit
+    // lane offset; rows past M or N are clamped to the last row (never
+    // stored).
+    const int drow = lane >> 3, dphys = lane & 7;
     uint32_t aoffs[kDmaA], boffs[kDmaB];
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i) {
         const int blk = wid * kDmaA + i, row = blk * 8 + drow;
         const int r_ = min(bm + row, M - 1) - bm;
-        aoffs[i] = static_cast<uint32_t>(r_) * static_cast<uint32_t>(K) + 16u * (dphys ^ (blk & 1));
+        aoffs[i] = static_cast<uint32_t>(r_) * static_cast<uint32_t>(K) + 16u * (dphys ^ lds_swz(row));
     }
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
         const int blk = wid * kDmaB + i, row = blk * 8 + drow;
         const int r_ = min(bn + row, N - 1) - bn;
-        boffs[i] = static_cast<uint32_t>(r_) * static_cast<uint32_t>(K) + 16u * (dphys ^ (blk & 1));
+        boffs[i] = static_cast<uint32_t>(r_) * static_cast<uint32_t>(K) + 16u * (dphys ^ lds_swz(row));
     }
     const int8_t *abase = q + static_cast<int64_t>(bm) * K;
     const int8_t *bbase = codes + static_cast<int64_t>(bn) * K;
-    // load j (0..5) of stage ks: 4 activation blocks, then 2 weight blocks
+    // load j of stage ks: kDmaA activation blocks, then kDmaB weight blocks.
+    // Stages past the end re-load the last stage (in bounds) into a buffer
+    // nobody reads again, which keeps every wait count below uniform.
     auto issue_load = [&](int ks, int j) {
+        const int kc = min(ks, NK - 1);
         const int buf = ks % kStages;
         if (j < kDmaA)
-            g2lds_16(abase + static_cast<int64_t>(ks) * kKC + aoffs[j], &As[buf][(wid * kDmaA + j) * 1024]);
+            dma16(abase + static_cast<int64_t>(kc) * kKC, aoffs[j],
+                  lds_offset(&As[buf][(wu * kDmaA + j) * 1024]));
         else
-            g2lds_16(bbase + static_cast<int64_t>(ks) * kKC + boffs[j - kDmaA],
-                     &Bs[buf][(wid * kDmaB + j - kDmaA) * 1024]);
+            dma16(bbase + static_cast<int64_t>(kc) * kKC, boffs[j - kDmaA],
+                  lds_offset(&Bs[buf][(wu * kDmaB + j - kDmaA) * 1024]));
     };
     auto issue_stage = [&](int ks) {
 #pragma unroll
@@ -127,181 +144,208 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
     };
 
     // ---- per-lane output columns and their group scales
-    int ncol[2];
-    bool nval[2];
+    int ncol[kTN];
+    bool nval[kTN];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        ncol[t] = bn + wn * 64 + t * 32 + li;
+    for (int t = 0; t < kTN; ++t) {
+        ncol[t] = bn + wn * kWTN + t * 32 + li;
         nval[t] = ncol[t] < N;
     }
     constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;
     // scale of column c, group g: byte offset (c G + g) ESZ of gscale; the
-    // wave's lane l fetches the aligned dword holding column wn*64 + l's
+    // wave's lane l fetches the aligned dword holding column wn*kWTN + l's
     // (the dword is moved back to end at the array's end if it would run past
     // it; the launcher guarantees the array holds at least 4 bytes)
-    const int64_t sc_col = static_cast<int64_t>(min(bn + wn * 64 + lane, N - 1)) * G;
+    const int64_t sc_col = static_cast<int64_t>(min(bn + wn * kWTN + lane, N - 1)) * G;
     const int64_t sc_last = static_cast<int64_t>(N) * G * ESZ - 4;
     auto dword_of = [&](int64_t byte) { return min(byte & ~static_cast<int64_t>(3), sc_last); };
     auto issue_scales = [&](int g) {
-        g2lds_dword(static_cast<const uint8_t *>(gscale) + dword_of((sc_col + g) * ESZ),
-                    &Ss[g % kStages][wid][0]);
+        dma4(gscale, static_cast<uint32_t>(dword_of((sc_col + g) * ESZ)),
+             lds_offset(&Ss[g % kStages][wu][0]));
     };
-    // the two scales this lane folds for group g, read after that group's
-    // scale loads are known to have landed
-    auto read_scales = [&](int g, float (&sc)[2]) {
-        uint32_t w0, w1;
-        const uint32_t base = lds_offset(&Ss[g % kStages][wid][0]);
-        asm volatile(
-            "ds_read_b32 %0, %2\n\t"
-            "ds_read_b32 %1, %3\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(w0), "=&v"(w1)
-            : "v"(base + 4 * li), "v"(base + 4 * (32 + li))
-            : "memory");
-        const uint32_t w[2] = {w0, w1};
+    // the scales this lane folds for group g, read after that group's scale
+    // loads are known to have landed
+    auto read_scales = [&](int g, float (&sc)[kTN]) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < kTN; ++t) {
+            const uint32_t w = Ss[g % kStages][wid][32 * t + li];
             const int64_t c = static_cast<int64_t>(nval[t] ? ncol[t] : N - 1);
             const int64_t byte = (c * G + g) * ESZ;
             const int shift = static_cast<int>(byte - dword_of(byte)) * 8;
             if constexpr (FMT == kFmtU8)
-                sc[t] = static_cast<float>((w[t] >> shift) & 0xFFu);
+                sc[t] = static_cast<float>((w >> shift) & 0xFFu);
             else
-                sc[t] = bf16_to_f32(static_cast<uint16_t>((w[t] >> shift) & 0xFFFFu));
+                sc[t] = bf16_to_f32(static_cast<uint16_t>((w >> shift) & 0xFFFFu));
         }
     };
 
-    v16i P[2][2];
-    float F[2][2][16];
+    // Partials are double-buffered by group parity: group g accumulates into
+    // P[g & 1] while the previous group's P[(g & 1) ^ 1] is folded into F one
+    // tile at a time, spread over group g's k-steps.  Folding a whole group
+    // at its boundary would stall the matrix cores behind a burst of VALU
+    // work (both waves of a SIMD reach the boundary together).
+    v16i P[2][kTM][kTN];
+    float F[kTM][kTN][16];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < kTM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kTN; ++b) {
+            P[0][a][b] = v16i{};
+            P[1][a][b] = v16i{};
 #pragma unroll
             for (int e = 0; e < 16; ++e) F[a][b][e] = 0.0f;
+        }
 
     // element e of a 32x32 result sits at row 8 (e / 4) + 4 lq + e % 4, column li
-    auto write_partials = [&](int tm, int tn, int g) {
+    auto write_partials = [&](const v16i &p, int tm, int tn, int g) {
         if (!nval[tn]) return;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = bm + wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * lq + (e & 3);
-            if (m < M) partials[(static_cast<int64_t>(m) * N + ncol[tn]) * G + g] = P[tm][tn][e];
+            const int m = bm + wm * kWTM + tm * 32 + 8 * (e >> 2) + 4 * lq + (e & 3);
+            if (m < M) partials[(static_cast<int64_t>(m) * N + ncol[tn]) * G + g] = p[e];
         }
     };
-    auto fold = [&](int tm, int tn, float s) {
+    auto fold = [&](const v16i &p, int tm, int tn, float s) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) F[tm][tn][e] += static_cast<float>(P[tm][tn][e]) * s;
+        for (int e = 0; e < 16; ++e) F[tm][tn][e] += static_cast<float>(p[e]) * s;
     };
 
-    // LDS byte offsets of this lane's fragments at k-step 0 of a stage
-    // (k-step kk adds 256 * kk): rows of the wave's 32 x 32 tiles, chunk lq
-    int aoff[2], boff[2];
+    // LDS byte offsets of this lane's fragments at k-step 0 of a stage: rows
+    // of the wave's 32 x 32 tiles, chunk lq.  K-step kk reads chunk
+    // 2 kk + lq, i.e. the k-step 0 offset XOR 32 kk (the swizzle is an XOR
+    // on the chunk index and 2 kk, lq occupy disjoint bits).
+    int aoff[kTM], boff[kTN];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        aoff[t] = lds_row_base(wm * 64 + t * 32 + li, lq);
-        boff[t] = lds_row_base(wn * 64 + t * 32 + li, lq);
-    }
+    for (int t = 0; t < kTM; ++t) aoff[t] = lds_chunk_addr(wm * kWTM + t * 32 + li, lq);
+#pragma unroll
+    for (int t = 0; t < kTN; ++t) boff[t] = lds_chunk_addr(wn * kWTN + t * 32 + li, lq);
 
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) P[a][b] = v16i{};
-
-    // Issue order (all vector-memory operations are direct LDS loads, so the
-    // only waits are the explicit ones below):
-    //   head format (one stage per group): group g's scales are issued in
-    //     stage g - 1 (group 0's before stage 0), ahead of that stage's load;
-    //   u8 format (two stages per group): group g's scales are issued in the
-    //     group's first stage, ahead of that stage's load.
-    // Either way they land before the stage whose wait precedes their fold.
-    if constexpr (SPG == 1) issue_scales(0);
+    // Issue order (every vector-memory operation of the loop is a direct LDS
+    // load issued from asm, so the only waits are the explicit ones below):
+    //   one stage per group (head format): group g's scales are issued in
+    //     stage g - 1 after that stage's barrier (group 0's between the two
+    //     prologue stages);
+    //   two stages per group (u8 format): group g's scales are issued in the
+    //     group's first stage after its barrier.
+    // Either way they are issued before the loads of the stage whose wait
+    // precedes their fold, and in-order completion does the rest.
     issue_stage(0);
-    if (NK > 1) issue_stage(1);
+    if constexpr (SPG == 1) issue_scales(0);
+    issue_stage(1);
 
-    for (int ks = 0; ks < NK; ++ks) {
-        const int st = (SPG == 1) ? 0 : (ks & 1);      // stage within its group
-        const int g = (SPG == 1) ? ks : (ks >> 1);
-        // stage ks has landed once no more than the loads issued after it
-        // are pending: the next stage's 6, plus one scale load if the
-        // previous stage issued one
-        if (ks + 1 >= NK) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (ks == 0) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStage) : "memory");
-        else if (SPG == 1 || st == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStage + 1) : "memory");
-        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStage) : "memory");
-        // all waves' loads of stage ks are in LDS, and all waves are done
-        // reading stage ks - 1, whose buffer the next issue overwrites
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if constexpr (SPG == 1) {
-            if (g + 1 < G) issue_scales(g + 1);
-        } else {
-            if (st == 0) issue_scales(g);
-        }
-        const bool more = ks + 2 < NK;
-        const bool fold_now = st == 0 && g > 0;
-        float scf[2] = {0.0f, 0.0f};
-        if (fold_now) read_scales(g - 1, scf);
-        const uint32_t Ab = lds_offset(As[ks % kStages]);
-        const uint32_t Bb = lds_offset(Bs[ks % kStages]);
+    constexpr int kSteps = kKC / 32;                   // k-steps per stage
+    constexpr int kTiles = kTM * kTN;
+    constexpr int kFoldEvery = SPG * kSteps / kTiles;  // k-steps between tile folds
+    static_assert(kFoldEvery >= 1 && kFoldEvery * kTiles == SPG * kSteps, "fold schedule");
+
+    // one group; H = g & 1 picks the partial buffer it accumulates into
+    auto run_group = [&](int g, auto h_const) {
+        constexpr int H = decltype(h_const)::value;
+        float scf[kTN] = {};            // previous group's scales (zero before group 0)
 #pragma unroll
-        for (int kk = 0; kk < kKC / 32; ++kk) {
-            v4i a[2], b[2];
-            lds_read4_b128(a[0], a[1], b[0], b[1], Ab + aoff[0] + 256 * kk,
-                           Ab + aoff[1] + 256 * kk, Bb + boff[0] + 256 * kk,
-                           Bb + boff[1] + 256 * kk);
+        for (int st = 0; st < SPG; ++st) {
+            const int ks = g * SPG + st;
+            // stage ks has landed once no more than the loads issued after
+            // it are pending: the next stage's kDmaPerStage, plus one scale
+            // load if one was issued between them
+            if (SPG == 1 || st == 1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStage + 1) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaPerStage) : "memory");
+            // all waves' loads of stage ks are in LDS, and all waves are done
+            // reading stage ks - 1, whose buffer the next issue overwrites
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if constexpr (SPG == 1) issue_scales(min(g + 1, G - 1));
+            else if (st == 0) issue_scales(g);
+            if (st == 0 && g > 0) read_scales(g - 1, scf);
+            const int8_t *Ab = As[ks % kStages];
+            const int8_t *Bb = Bs[ks % kStages];
+            // opaque per stage: keeps the per-k-step XORs below in the loop
+            // instead of 16 hoisted, always-live address registers
 #pragma unroll
-            for (int tm = 0; tm < 2; ++tm)
+            for (int t = 0; t < kTM; ++t) asm volatile("" : "+v"(aoff[t]));
 #pragma unroll
-                for (int tn = 0; tn < 2; ++tn) {
-                    if (kk == 0 && st == 0) {
-                        // fold group g - 1 (all zero when g == 0), restart P
-                        if constexpr (WRITE_P) {
-                            if (g > 0) write_partials(tm, tn, g - 1);
-                        }
-                        fold(tm, tn, scf[tn]);
-                        P[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[tm], b[tn], v16i{}, 0, 0, 0);
-                    } else {
-                        P[tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[tm], b[tn], P[tm][tn], 0, 0, 0);
+            for (int t = 0; t < kTN; ++t) asm volatile("" : "+v"(boff[t]));
+            // fragments double-buffered across k-steps: k-step kk + 1's LDS
+            // reads are in flight while k-step kk's matrix ops run
+            v4i fa[2][kTM], fb[2][kTN];
+            auto read_frags = [&](int kk, v4i(&a)[kTM], v4i(&b)[kTN]) {
+#pragma unroll
+                for (int t = 0; t < kTM; ++t) a[t] = *reinterpret_cast<const v4i *>(Ab + (aoff[t] ^ (32 * kk)));
+#pragma unroll
+                for (int t = 0; t < kTN; ++t) b[t] = *reinterpret_cast<const v4i *>(Bb + (boff[t] ^ (32 * kk)));
+            };
+            read_frags(0, fa[0], fb[0]);
+#pragma unroll
+            for (int kk = 0; kk < kSteps; ++kk) {
+                const int pos = st * kSteps + kk;      // k-step within the group
+                if (kk + 1 < kSteps) read_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+                for (int tm = 0; tm < kTM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < kTN; ++tn) {
+                        const v4i a = fa[kk & 1][tm], b = fb[kk & 1][tn];
+                        P[H][tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            a, b, pos == 0 ? v16i{} : P[H][tm][tn], 0, 0, 0);
                     }
+                // fold one tile of the previous group (zeros before group 1)
+                if (pos % kFoldEvery == 0) {
+                    const int t = pos / kFoldEvery, tm = t / kTN, tn = t % kTN;
+                    if constexpr (WRITE_P) {
+                        if (g > 0) write_partials(P[H ^ 1][tm][tn], tm, tn, g - 1);
+                    }
+                    fold(P[H ^ 1][tm][tn], tm, tn, scf[tn]);
                 }
-            // the next-but-one stage's loads, spread over the k-steps so a
-            // full memory queue delays a few matrix ops, not the whole stage
-            if (more && kk < 3) {
-                issue_load(ks + 2, 2 * kk);
-                issue_load(ks + 2, 2 * kk + 1);
+                // the next-but-one stage's loads, spread over the k-steps so
+                // a full memory queue delays a few matrix ops, not a stage
+                if (kk < 3) {
+#pragma unroll
+                    for (int j = 0; j < kDmaPerStage / 3; ++j) issue_load(ks + 2, (kDmaPerStage / 3) * kk + j);
+                }
             }
         }
+    };
+    for (int g = 0; g < G; g += 2) {
+        run_group(g, std::integral_constant<int, 0>{});
+        if (g + 1 < G) run_group(g + 1, std::integral_constant<int, 1>{});
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last group's scales
+    // every load has landed (the re-loads past the end included: nothing may
+    // still write this workgroup's LDS once its waves end)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     {
-        float scf[2];
+        float scf[kTN];
         read_scales(G - 1, scf);
+        auto fold_last = [&](auto h_const) {
+            constexpr int H = decltype(h_const)::value;
 #pragma unroll
-        for (int tm = 0; tm < 2; ++tm)
+            for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn) {
-                if constexpr (WRITE_P) write_partials(tm, tn, G - 1);
-                fold(tm, tn, scf[tn]);
-            }
+                for (int tn = 0; tn < kTN; ++tn) {
+                    if constexpr (WRITE_P) write_partials(P[H][tm][tn], tm, tn, G - 1);
+                    fold(P[H][tm][tn], tm, tn, scf[tn]);
+                }
+        };
+        if ((G - 1) & 1) fold_last(std::integral_constant<int, 1>{});
+        else fold_last(std::integral_constant<int, 0>{});
     }
 
-    float rn[2];
+    float rn[kTN];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kTN; ++t) {
         rn[t] = 0x1p-7f;
         if constexpr (FMT == kFmtU8)
             if (nval[t]) rn[t] = bf16_to_f32(rscale[ncol[t]]) * 0x1p-7f;
     }
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm)
+    for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int m = bm + wm * 64 + tm * 32 + 8 * (e >> 2) + 4 * lq + (e & 3);
+            const int m = bm + wm * kWTM + tm * 32 + 8 * (e >> 2) + 4 * lq + (e & 3);
             if (m >= M) continue;
             const float sm = scale[m];
 #pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
+            for (int tn = 0; tn < kTN; ++tn)
                 if (nval[tn]) y[static_cast<int64_t>(m) * N + ncol[tn]] = F[tm][tn][e] * (sm * rn[tn]);
         }
 }

@@ -138,6 +138,44 @@ __device__ __forceinline__ void lds_read4_b128(v4i &r0, v4i &r1, v4i &r2, v4i &r
         : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
         : "memory");
 }
+__device__ __forceinline__ void lds_read2_b128(v4i &r0, v4i &r1, uint32_t a0, uint32_t a1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1)
+        : "v"(a0), "v"(a1)
+        : "memory");
+}
+// Direct global -> LDS loads issued from inline asm.  Same data movement as
+// g2lds_16 / g2lds_dword, but invisible to the compiler's wait-count pass:
+// it therefore neither drains these loads before every later LDS read (as it
+// must for the builtin, not knowing which LDS bytes the load writes) nor
+// tracks them at all.  Callers order them with explicit vmcnt waits and
+// barriers.  Source = sbase (wave-uniform) + voff (per lane, unsigned 32-bit);
+// destination = LDS byte address lds (wave-uniform, passed in M0) + size *
+// lane.  The compiler's hazard checks do not look inside asm, so the block
+// starts with the 5 wait states the ISA requires between a VALU write of an
+// SGPR (v_readlane / v_readfirstlane, e.g. reloading a spilled base address)
+// and a vector memory instruction reading that SGPR; they also cover the one
+// an M0 write needs before an LDS DMA.  No register outputs, so nothing is
+// live while the load is in flight.
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "{m0}"(lds)
+        : "memory");
+}
+__device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "{m0}"(lds)
+        : "memory");
+}
 // LDS byte offset of a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));

@@ -48,6 +48,18 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=None,
+                    help="run a plain f32 negate kernel that reads BYTES and writes BYTES "
+                         "(5 launches) and exit: the reference for scaling rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-from", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from rocprofv3 --pmc "
+                         "counter_collection CSVs (kernel chosen by --kernel-match) and exit")
+    ap.add_argument("--kernel-match", default=None,
+                    help="substring of the dominant kernel's name, for --traffic-from")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30,
+                    help="the BYTES the copy-calibration CSVs were taken with")
     return ap.parse_args()
 
 
@@ -85,8 +97,80 @@ def load_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(nbytes):
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+
+
+def _counter_means(path, match):
+    """Mean counter value per dispatch of the kernels whose name contains `match`."""
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if match in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no dispatch of a kernel matching %r in %s" % (match, path))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def traffic_from(args):
+    """profiles/traffic_<workload>.json: HBM bytes per launch of the dominant
+    kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the
+    bytes a plain copy of known size really moves per KiB the counter reports."""
+    from rotated_w8a8_int8_amd import workloads as W
+    wl = W.WORKLOADS[args.workload]
+    sz = sizes(wl)
+    if not args.kernel_match:
+        raise SystemExit("--traffic-from needs --kernel-match")
+    f_csv, w_csv, cf_csv, cw_csv = args.traffic_from
+    fetch, nf = _counter_means(f_csv, args.kernel_match)
+    write, nw = _counter_means(w_csv, args.kernel_match)
+    cfetch, _ = _counter_means(cf_csv, "neg")
+    cwrite, _ = _counter_means(cw_csv, "neg")
+    fetch_scale = args.copy_bytes / (cfetch["FETCH_SIZE"] * 1024.0)
+    write_scale = args.copy_bytes / (cwrite["WRITE_SIZE"] * 1024.0)
+    fbytes = fetch["FETCH_SIZE"] * 1024.0 * fetch_scale
+    wbytes = write["WRITE_SIZE"] * 1024.0 * write_scale
+    fused = wl.M == 1 and wl.K <= 20480
+    alg = sz["step"] + wl.M * wl.K + wl.M * 4 if fused else sz["contraction"]
+    rec = {
+        "workload": wl.name,
+        "kernel_match": args.kernel_match,
+        "dispatches": {"fetch": nf["FETCH_SIZE"], "write": nw["WRITE_SIZE"]},
+        "fetch_kib_per_dispatch": round(fetch["FETCH_SIZE"], 1),
+        "write_kib_per_dispatch": round(write["WRITE_SIZE"], 1),
+        "copy_bytes_each_way": args.copy_bytes,
+        "copy_fetch_kib": round(cfetch["FETCH_SIZE"], 1),
+        "copy_write_kib": round(cwrite["WRITE_SIZE"], 1),
+        "fetch_scale": round(fetch_scale, 4),
+        "write_scale": round(write_scale, 4),
+        "bytes_per_launch": int(round(fbytes + wbytes)),
+        "fetch_bytes_per_launch": int(round(fbytes)),
+        "write_bytes_per_launch": int(round(wbytes)),
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": round((fbytes + wbytes) / alg, 4),
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -99,6 +183,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     B.lib()                                            # fail loudly if not built
 
     wl = W.WORKLOADS[args.workload]

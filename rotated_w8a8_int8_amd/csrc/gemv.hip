@@ -14,11 +14,11 @@
 //                    rotation and quantisation of the token.  For the u8 format
 //                    the epilogue is exact integer arithmetic up to one f64
 //                    product, rounded once.
-//   skinny_kernel    2 <= M <= 128.  Each wave owns 16 weight rows and streams
-//                    them straight from HBM into the B operand of
-//                    v_mfma_i32_16x16x64_i8; the activation codes of all M
-//                    tokens are staged per K group in LDS and shared by the
-//                    workgroup's 4 waves.
+//   skinny_kernel    2 <= M <= 128.  Each compute wave owns 16 weight rows and
+//                    streams them straight from HBM into the B operand of
+//                    v_mfma_i32_16x16x64_i8 with several stages in flight; a
+//                    producer wave stages the activation codes of all M
+//                    tokens in LDS for the workgroup.
 #include <algorithm>
 
 #include "rad_device.h"
@@ -333,133 +333,214 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 }
 
 // ------------------------------------------------------- 2 <= M <= 128 ----
-// Workgroup = 4 waves = 64 weight rows.  Lane L = j + 16 qd of a wave holds,
-// for MFMA step st of a K group, bytes [64 st + 16 qd, +16) of weight row
-// n0 + j (B operand) and of token mb*16 + j (A operand, from LDS).  Both
-// operands use the same byte-to-k assignment, so each MFMA sums exactly the
-// 64 products of its step.  The int32 result D[i][j] sits in lane
-// j + 16 (i / 4), element i % 4: token mb*16 + 4 qd + e, weight row n0 + j.
-template <int FMT, int MB, bool WRITE_P>
-__global__ __launch_bounds__(256) void skinny_kernel(const int8_t *__restrict__ q,
-                                                     const float *__restrict__ scale,
-                                                     const int8_t *__restrict__ codes,
-                                                     const void *__restrict__ gscale,
-                                                     const uint16_t *__restrict__ rscale,
-                                                     float *__restrict__ y,
-                                                     int32_t *__restrict__ partials, int M, int N,
-                                                     int K) {
-    constexpr int GW = (FMT == kFmtU8) ? 256 : 128;   // K bytes per group = per LDS stage
-    constexpr int SPG = GW / 64;                      // MFMA steps per group
-    constexpr int LDA = GW + 16;                      // padded LDS pitch (bytes)
-    constexpr int ROWS = MB * 16;
-    constexpr int CH = ROWS * GW / 16;                // 16-byte chunks per stage
-    constexpr int CPT = (CH + 255) / 256;             // chunks per thread
-    __shared__ __attribute__((aligned(16))) int8_t As[2][ROWS * LDA];
+// The weight stream is the cost (M <= 128 int8 MACs per weight byte is far
+// below the matrix units' ridge), so the kernel is built to keep HBM busy:
+//
+//   * A workgroup is kSkW compute waves plus one producer wave.  Compute wave
+//     w owns 16 weight rows and streams them from HBM straight into the B
+//     operand of v_mfma_i32_16x16x64_i8, keeping kSkD stages (128 bytes of K
+//     each) of its rows in flight in registers.
+//   * The producer wave copies the activation codes of all M tokens, one
+//     128-byte stage of K at a time, into a 3-deep LDS ring with direct
+//     global -> LDS loads, and the compute waves read their A operands from
+//     there.  A separate wave keeps these short, L2-resident loads out of the
+//     compute waves' in-order memory queue, where they would wait behind
+//     weight loads issued stages ahead.
+//   * One s_barrier per stage: the producer arrives once stage s has landed,
+//     the compute waves once they are done with stage s - 1, whose buffer the
+//     producer refills next.
+//
+// Lane L = j + 16 q of a compute wave holds, for k-step kk (64 bytes) of a
+// stage, bytes [64 kk + 16 q, +16) of weight row n0 + j (B) and of token
+// 16 mb + j (A).  Both operands use the same byte-to-k assignment, so each
+// MFMA sums exactly the 64 products of its k-step; P[mb] element e is token
+// 16 mb + 4 q + e, row n0 + j.  Each K group's partials are folded into f32
+// with the group scale once the group's stages are done.
+//
+// LDS: token row m of a stage occupies 128 bytes, its 16-byte chunk c stored
+// in slot c ^ swz(m), swz(m) = (m mod 8) ^ ((m / 8) mod 2): the 16 tokens one
+// read phase touches at a common chunk then hit 16 different bank groups,
+// while each producer load still reads whole 128-byte segments.
+constexpr int kSkStageK = 128;                  // K bytes per stage
+constexpr int kSkRing = 3;                      // activation stages in LDS
+constexpr int kSkD = 4;                         // weight stages in flight per wave
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int j = lane & 15;
-    const int qd = lane >> 4;
-    const int n0 = blockIdx.x * 64 + (tid >> 6) * 16;
+__device__ __forceinline__ int sk_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Workgroup shape per token block count: up to 64 tokens, 7 compute waves at
+// 4 waves per SIMD (<= 128 registers); above, 5 compute waves at 3 per SIMD,
+// which leaves room to read a whole k-step of A fragments before its matrix
+// ops (reading them one by one exposes the LDS latency on every MFMA).  Two
+// workgroups share a CU either way.
+template <int MB> struct SkShape {
+    static constexpr int W = MB <= 4 ? 7 : 5;          // compute waves
+    static constexpr int WPE = MB <= 4 ? 4 : 3;        // waves per SIMD
+    static constexpr int THREADS = 64 * (W + 1);       // plus the producer wave
+};
+
+template <int FMT, int MB, bool WRITE_P>
+__global__ __launch_bounds__(SkShape<MB>::THREADS) __attribute__((amdgpu_waves_per_eu(SkShape<MB>::WPE)))
+void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale,
+                   const int8_t *__restrict__ codes, const void *__restrict__ gscale,
+                   const uint16_t *__restrict__ rscale, float *__restrict__ y,
+                   int32_t *__restrict__ partials, int M, int N, int K) {
+    constexpr int MP = 16 * MB;                       // token rows, padded
+    constexpr int ABYTES = MP * kSkStageK;            // one activation stage
+    constexpr int GW = (FMT == kFmtU8) ? 256 : 128;   // K bytes per group
+    constexpr int SPG = GW / kSkStageK;               // stages per group
+    constexpr int NDMA = ABYTES / 1024;               // producer loads per stage
+    constexpr int kSkW = SkShape<MB>::W;
+    static_assert(kSkD % SPG == 0, "a ring turn holds whole groups");
+    __shared__ __attribute__((aligned(1024))) int8_t As[kSkRing][ABYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int NS = K / kSkStageK;
+    const int G = K / GW;
+    // Workgroups start their K walk at different groups (and wrap around),
+    // so the activation slice every producer reads at a given moment is not
+    // the same few cache lines on the same L2 channels across the GPU.
+    const int soff = SPG * (static_cast<int>(blockIdx.x) % G);
+    auto phys = [&](int s) { return (min(s, NS - 1) + soff) % NS; };   // past the end: re-read
+
+    if (wid == kSkW) {
+        // ---- producer.  Load i of a stage fills token rows 8 i .. 8 i + 7:
+        // lane l takes row 8 i + l / 8, slot l % 8, i.e. logical chunk
+        // (l % 8) ^ swz(row).  Token rows past M repeat row M - 1.
+        uint32_t offs[NDMA];
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int row = 8 * i + (lane >> 3);
+            const int r = min(row, M - 1);
+            offs[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(K) +
+                      16u * static_cast<uint32_t>((lane & 7) ^ sk_swz(row));
+        }
+        auto issue = [&](int s) {
+            const int buf = s % kSkRing;
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i)
+                dma16(q + static_cast<int64_t>(phys(s)) * kSkStageK, offs[i], lds_offset(&As[buf][i * 1024]));
+        };
+        issue(0);
+        if (NS > 1) issue(1);
+        for (int s = 0; s < NS; ++s) {
+            // stage s has landed once at most the next stage's loads remain
+            if (s + 1 < NS)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NDMA) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (s + 2 < NS) issue(s + 2);       // into the buffer of stage s - 1
+        }
+        return;
+    }
+
+    // ---- compute waves
+    const int j = lane & 15, qd = lane >> 4;
+    const int n0 = (blockIdx.x * kSkW + wid) * 16;
     const int nrow = n0 + j;
     const bool nvalid = nrow < N;
-    const int8_t *wrow = codes + static_cast<int64_t>(nvalid ? nrow : 0) * K + 16 * qd;
-    const int G = K / GW;
+    const int nr = min(nrow, N - 1);
+    const int8_t *wrow = codes + static_cast<int64_t>(nr) * K + 16 * qd;
 
-    auto load_b = [&](v4i (&b)[SPG], int g) {
+    auto load_w = [&](int s, v4i(&dst)[2]) {
+        const int64_t off = static_cast<int64_t>(phys(s)) * kSkStageK;
 #pragma unroll
-        for (int st = 0; st < SPG; ++st)
-            b[st] = nvalid ? ld16(wrow + static_cast<int64_t>(g) * GW + 64 * st) : v4i{0, 0, 0, 0};
+        for (int kk = 0; kk < 2; ++kk) dst[kk] = ld16(wrow + off + 64 * kk);
     };
-    auto load_a = [&](v4i (&ar)[CPT], int g) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + 256 * i;
-            const int row = idx / (GW / 16);
-            const int kb = (idx % (GW / 16)) * 16;
-            ar[i] = (idx < CH && row < M)
-                        ? ld16(q + static_cast<int64_t>(row) * K + static_cast<int64_t>(g) * GW + kb)
-                        : v4i{0, 0, 0, 0};
-        }
-    };
-    auto store_a = [&](const v4i (&ar)[CPT], int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < CH) {
-                const int row = idx / (GW / 16);
-                const int kb = (idx % (GW / 16)) * 16;
-                *reinterpret_cast<v4i *>(&As[buf][row * LDA + kb]) = ar[i];
-            }
-        }
-    };
-    auto load_scale = [&](int g) -> float {
-        if (!nvalid) return 0.0f;
+    // Group scales ride in the ring as raw bits and are converted only when
+    // folded: converting at load time would make the wave wait for the load
+    // right away, and with in-order completion that drains the whole ring.
+    auto load_scale = [&](int g) -> uint32_t {
+        const int64_t idx = static_cast<int64_t>(nr) * G + phys(SPG * g) / SPG;
         if constexpr (FMT == kFmtU8)
-            return static_cast<float>(static_cast<const uint8_t *>(gscale)[static_cast<int64_t>(nrow) * G + g]);
+            return static_cast<const uint8_t *>(gscale)[idx];
         else
-            return bf16_to_f32(static_cast<const uint16_t *>(gscale)[static_cast<int64_t>(nrow) * G + g]);
+            return static_cast<const uint16_t *>(gscale)[idx];
+    };
+    auto scale_value = [&](uint32_t raw) -> float {
+        if constexpr (FMT == kFmtU8)
+            return static_cast<float>(raw);
+        else
+            return bf16_to_f32(static_cast<uint16_t>(raw));
     };
 
+    v4i wr[kSkD][2];
+    uint32_t scr[kSkD / SPG];                         // scale bits of each group in the ring
+#pragma unroll
+    for (int i = 0; i < kSkD; ++i) {
+        load_w(i, wr[i]);
+        if (i % SPG == 0) scr[i / SPG] = load_scale(i / SPG);
+    }
+
+    v4i P[MB];
     float F[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+        P[mb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) F[mb][e] = 0.0f;
-
-    v4i bcur[SPG], bnext[SPG], ar[CPT];
-    load_b(bcur, 0);
-    load_a(ar, 0);
-    float sc = load_scale(0);
-    store_a(ar, 0);
-    __syncthreads();
-
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        const bool more = g + 1 < G;
-        float sc_next = 0.0f;
-        if (more) {
-            load_b(bnext, g + 1);
-            load_a(ar, g + 1);
-            sc_next = load_scale(g + 1);
-        }
-        v4i P[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) P[mb] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int st = 0; st < SPG; ++st) {
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const v4i af = *reinterpret_cast<const v4i *>(&As[buf][(mb * 16 + j) * LDA + 64 * st + 16 * qd]);
-                P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bcur[st], P[mb], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            F[mb][0] += static_cast<float>(P[mb].x) * sc;
-            F[mb][1] += static_cast<float>(P[mb].y) * sc;
-            F[mb][2] += static_cast<float>(P[mb].z) * sc;
-            F[mb][3] += static_cast<float>(P[mb].w) * sc;
-        }
-        if (WRITE_P && nvalid) {
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int pv[4] = {P[mb].x, P[mb].y, P[mb].z, P[mb].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = mb * 16 + 4 * qd + e;
-                    if (m < M) partials[(static_cast<int64_t>(m) * N + nrow) * G + g] = pv[e];
-                }
-            }
-        }
-        if (more) {
-            store_a(ar, buf ^ 1);
-#pragma unroll
-            for (int st = 0; st < SPG; ++st) bcur[st] = bnext[st];
-            sc = sc_next;
-        }
-        __syncthreads();
     }
+
+    // the LDS byte offset of this lane's A chunk c of token row 16 mb + j
+    auto a_off = [&](int mb, int c) {
+        const int row = 16 * mb + j;
+        return 128 * row + 16 * (c ^ sk_swz(row));
+    };
+
+    // one stage: s the stage, i = s mod kSkD its ring slot (a constant after
+    // unrolling)
+    auto stage = [&](int s, int i) {
+        __builtin_amdgcn_s_barrier();                 // stage s is in LDS
+        asm volatile("" ::: "memory");
+        const int8_t *Ab = As[s % kSkRing];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            v4i a[MB];                                // the k-step's A fragments, read together
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + a_off(mb, 4 * kk + qd));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb], wr[i][kk], P[mb], 0, 0, 0);
+        }
+        load_w(s + kSkD, wr[i]);                      // refill the slot just used
+        if (i % SPG == SPG - 1) {
+            // the group ends here: fold it, then refill its scale slot
+            const int g = phys(s) / SPG;              // the K group just completed
+            // opaque here, after this stage's barrier: keeps the scheduler
+            // from converting (and so waiting for) the scale any earlier
+            uint32_t raw = scr[i / SPG];
+            asm volatile("" : "+v"(raw));
+            const float sc = scale_value(raw);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                if constexpr (WRITE_P) {
+                    if (nvalid) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int m = 16 * mb + 4 * qd + e;
+                            if (m < M) partials[(static_cast<int64_t>(m) * N + nrow) * G + g] = P[mb][e];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) F[mb][e] += static_cast<float>(P[mb][e]) * sc;
+                P[mb] = v4i{0, 0, 0, 0};
+            }
+            scr[i / SPG] = load_scale(s / SPG + kSkD / SPG);
+        }
+    };
+    // Whole ring turns in a branch-free loop (so the compiler's wait counts
+    // keep kSkD stages in flight across the back edge), then the remainder.
+    const int NSm = NS - NS % kSkD;
+    for (int s0 = 0; s0 < NSm; s0 += kSkD) {
+#pragma unroll
+        for (int i = 0; i < kSkD; ++i) stage(s0 + i, i);
+    }
+#pragma unroll
+    for (int i = 0; i < kSkD; ++i)
+        if (NSm + i < NS) stage(NSm + i, i);
 
     if (!nvalid) return;
     float rn = 0x1p-7f;
@@ -468,7 +549,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t *__restrict__ 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int m = mb * 16 + 4 * qd + e;
+            const int m = 16 * mb + 4 * qd + e;
             if (m < M) y[static_cast<int64_t>(m) * N + nrow] = F[mb][e] * (scale[m] * rn);
         }
 }
@@ -476,10 +557,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(const int8_t *__restrict__ 
 template <int FMT, int MB>
 hipError_t launch_skinny_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                            int32_t *P, hipStream_t st) {
-    const int grid = static_cast<int>((w.N + 63) / 64);
+    const int64_t rows_per_wg = 16 * SkShape<MB>::W;
+    const int grid = static_cast<int>((w.N + rows_per_wg - 1) / rows_per_wg);
     auto kern = P ? skinny_kernel<FMT, MB, true> : skinny_kernel<FMT, MB, false>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, q, s, w.codes, w.gscale, w.rscale, y, P,
-                       static_cast<int>(M), static_cast<int>(w.N), static_cast<int>(w.K));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(SkShape<MB>::THREADS), 0, st, q, s, w.codes, w.gscale, w.rscale, y,
+                       P, static_cast<int>(M), static_cast<int>(w.N), static_cast<int>(w.K));
     return hipGetLastError();
 }
 

@@ -358,14 +358,16 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 // with the group scale once the group's stages are done.
 //
 // LDS: token row m of a stage occupies 128 bytes, its 16-byte chunk c stored
-// in slot c ^ swz(m), swz(m) = (m mod 8) ^ ((m / 8) mod 2): the 16 tokens one
-// read phase touches at a common chunk then hit 16 different bank groups,
-// while each producer load still reads whole 128-byte segments.
+// in slot c ^ (m mod 8).  With the 16x16x64 operand layout (lane j + 16 q
+// reads token j, chunk q of the k-step) this measures free of bank conflicts
+// (SQ_LDS_BANK_CONFLICT = 0); the variant that also flips by (m / 8) mod 2
+// measured 2-way conflicts.  Each producer load still reads whole 128-byte
+// segments.
 constexpr int kSkStageK = 128;                  // K bytes per stage
 constexpr int kSkRing = 3;                      // activation stages in LDS
 constexpr int kSkD = 4;                         // weight stages in flight per wave
 
-__device__ __forceinline__ int sk_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int sk_swz(int row) { return row & 7; }
 
 // Workgroup shape per token block count: up to 64 tokens, 7 compute waves at
 // 4 waves per SIMD (<= 128 registers); above, 5 compute waves at 3 per SIMD,

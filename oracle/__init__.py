@@ -69,8 +69,9 @@ def _load():
         lib.orc_group_partials.argtypes = [p, p, p, i64, i64, i64, ci]
         lib.orc_epilogue.argtypes = [p, p, ci, p, p, p, i64, i64, i64]
         lib.orc_linear.argtypes = [p, p, p, ci, p, p, p, i64, i64, i64]
+        lib.orc_quant_weight_i8.argtypes = [p, p, p, p, i64, i64, ci]
         for f in (lib.orc_fwht128, lib.orc_quant_act_i8, lib.orc_group_partials,
-                  lib.orc_epilogue, lib.orc_linear):
+                  lib.orc_epilogue, lib.orc_linear, lib.orc_quant_weight_i8):
             f.restype = ci
         _lib = lib
     return _lib
@@ -165,3 +166,27 @@ def forward(x: np.ndarray, qw: np.ndarray, fmt: int, gscale: np.ndarray,
     """The whole layer: rotate + quantise ``x``, then contract.  Returns (q, s, y)."""
     q, s = quant_act_i8(x, rotate=True)
     return q, s, linear(q, s, qw, fmt, gscale, rscale)
+
+
+# Scale candidates of the searched round-to-nearest weight quantiser (reading
+# R8 in rad_oracle.c): alpha_c = (64 - c) / 64, c = 0..15.
+WQ_CANDIDATES = 16
+
+
+def quant_weight_i8(W: np.ndarray, fmt: int):
+    """Rotate float weights ``W`` [N][K] per 128-block and quantise them to int8
+    with a searched scale per group.  Returns (codes int8 [N][K], gscale
+    (uint8 [N][K/256] or bf16 bits uint16 [N][K/128]), rscale (bf16 bits
+    uint16 [N] for the u8 format, else None))."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    G = K // GROUP_WIDTH[fmt]
+    codes = np.empty((N, K), np.int8)
+    if fmt == FMT_U8G256_BF16ROW:
+        gscale = np.empty((N, G), np.uint8)
+        rscale = np.empty((N,), np.uint16)
+    else:
+        gscale = np.empty((N, G), np.uint16)
+        rscale = None
+    _check(_load().orc_quant_weight_i8(_ptr(W), _ptr(codes), _ptr(gscale), _ptr(rscale), N, K, fmt))
+    return codes, gscale, rscale

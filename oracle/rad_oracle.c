@@ -46,6 +46,7 @@
 #include <math.h>
 #include <fenv.h>
 #include <omp.h>
+#include <stdlib.h>
 
 #define ORC_OK           0
 #define ORC_E_ARG       -1   /* a size, pointer or format is invalid      */
@@ -262,5 +263,177 @@ int orc_linear(const int8_t *qx, const float *s, const int8_t *qw, int fmt,
                                        (const char *)gscale + (size_t)(n * G) * esz,
                                        fmt == ORC_FMT_U8G256_BF16ROW ? rscale + n : NULL);
         }
+    return status;
+}
+
+/*
+ * ---- Weight-side round-to-nearest quantiser with a searched scale ----
+ *
+ * Source: the recipe rules of section "How this file was made" on the model
+ * cards "Qwen3.8-Flash-Next, IQR-V4 -- radiance container" (rules "rtn
+ * codes=i8 group=128 scale=bf16 transform=fwht128 clamp=sym rule=search",
+ * and its table row "Trunk": a scale per 128 columns searched for least
+ * error) and "Qwen3.8-27B IQ8R + DFlash2 -- radiance container" (trunk rules
+ * with int8 codes, group 256, u8 scales under a bf16 second scale per row,
+ * block2=1x*, fwht128, clamp=sym, rule=search).  The card fits the trunk by
+ * GPTQ; what is restated here is the round-to-nearest form of the same format
+ * (no Hessians).  Readings where the cards are silent:
+ *   R7  The weight rows are rotated like activations: every 128-block of a
+ *       row by v -> v.H (reading R3's butterfly order), so that
+ *       x.W^T = (x.H).(W.H)^T / 128.
+ *   R8  "rule=search" picks, per group, the candidate scale with the least
+ *       squared error sum_k (w~_k - scale * q_k)^2 over the group.  The
+ *       candidates are alpha_c * amax / 127 for alpha_c = (64 - c) / 64,
+ *       c = 0..15 (no clipping, then clipping by up to 15/64 of the range);
+ *       amax is the group's largest |w~|.  Ties go to the smaller c.
+ *   R9  Codes for a scale d are clamp(rne(w~ / d), -127, 127) (f32 division,
+ *       ties to even; "clamp=sym" keeps -128 out); d = 0 gives code 0.  The
+ *       error term e = w~ - d * q is exact in f64; e * e and the group sum are
+ *       f64, the sum taken as a balanced pairwise tree over the group in
+ *       index order (pairs of neighbours, then pairs of pairs, ...).
+ *   R10 Head format: the stored scale is bf16_rne(alpha_c * amax / 127)
+ *       (f32 product, then f32 division by 127, then rounding to bf16), and
+ *       d is its value.  u8 format: the row scale is r = bf16_rne((amax_row /
+ *       127) / 255) with amax_row the row's largest |w~| (so u8 = 255 can
+ *       carry it); candidate c of group g has u8 = clamp(rne((alpha_c *
+ *       amax_g / 127) / r), 1, 255) and d = r * u8 (exact in f32).  r = 0
+ *       (an all-zero row) stores u8 = 1 and zero codes.
+ */
+#define ORC_WQ_CANDIDATES 16
+
+static float wq_alpha(int c) { return (float)(64 - c) / 64.0f; }
+
+/* f32 -> bf16 bits, round to nearest, ties to even (finite input). */
+static uint16_t bf16_rne_bits(float f)
+{
+    union { uint32_t u; float f; } c;
+    c.f = f;
+    uint32_t lsb = (c.u >> 16) & 1u;
+    return (uint16_t)((c.u + 0x7FFFu + lsb) >> 16);
+}
+
+static float bf16_float(uint16_t bits)
+{
+    union { uint32_t u; float f; } c;
+    c.u = (uint32_t)bits << 16;
+    return c.f;
+}
+
+static int8_t wq_code(float w, float d)
+{
+    if (d == 0.0f) return 0;
+    float r = rintf(w / d);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* Pairwise f64 sum of (w[i] - d q[i])^2 over n (a power of two) elements. */
+static double wq_sq_err(const float *w, const int8_t *q, float d, int64_t n)
+{
+    if (n == 1) {
+        double e = (double)w[0] - (double)d * (double)q[0];
+        return e * e;
+    }
+    return wq_sq_err(w, q, d, n / 2) + wq_sq_err(w + n / 2, q + n / 2, d, n / 2);
+}
+
+/*
+ * Quantise float weights W [N][K] (row-major, K % group == 0): rotate (R7),
+ * then pick scales (R8-R10).  codes int8 [N][K]; gscale u8 [N][K/256] or bf16
+ * bits [N][K/128]; rscale bf16 bits [N] for the u8 format (ignored, may be
+ * NULL, for the head format).
+ */
+int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
+                        int64_t N, int64_t K, int fmt)
+{
+    int64_t gw = group_width(fmt);
+    if (!W || !codes || !gscale || gw == 0 || N < 0 || K <= 0 || K % gw != 0) return ORC_E_ARG;
+    if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
+    if (fegetround() != FE_TONEAREST) return ORC_E_ROUNDING;
+    int64_t G = K / gw;
+    int status = ORC_OK;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < N; ++n) {
+        float *wr = (float *)malloc((size_t)K * sizeof(float));
+        int8_t *qc = (int8_t *)malloc((size_t)gw);
+        if (!wr || !qc) {
+            free(wr);
+            free(qc);
+            #pragma omp critical
+            status = ORC_E_ARG;
+            continue;
+        }
+        int bad = 0;
+        for (int64_t k = 0; k < K; ++k) {
+            wr[k] = W[n * K + k];
+            if (!isfinite(wr[k])) bad = 1;
+        }
+        if (bad) {
+            free(wr);
+            free(qc);
+            #pragma omp critical
+            status = ORC_E_NONFINITE;
+            continue;
+        }
+        for (int64_t c = 0; c < K; c += 128) fwht128_block(wr + c);
+        float amax_row = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(wr[k]);
+            if (a > amax_row) amax_row = a;
+        }
+        float r = 0.0f;
+        if (fmt == ORC_FMT_U8G256_BF16ROW) {
+            uint16_t rb = bf16_rne_bits((amax_row / 127.0f) / 255.0f);
+            rscale[n] = rb;
+            r = bf16_float(rb);
+        }
+        for (int64_t g = 0; g < G; ++g) {
+            const float *wg = wr + g * gw;
+            int8_t *out = codes + n * K + g * gw;
+            float amax = 0.0f;
+            for (int64_t k = 0; k < gw; ++k) {
+                float a = fabsf(wg[k]);
+                if (a > amax) amax = a;
+            }
+            double best_err = 0.0;
+            int best = -1;
+            uint16_t best_scale = 0;
+            for (int c = 0; c < ORC_WQ_CANDIDATES; ++c) {
+                float target = (amax * wq_alpha(c)) / 127.0f;
+                uint16_t stored;
+                float d;
+                if (fmt == ORC_FMT_U8G256_BF16ROW) {
+                    float u = 1.0f;
+                    if (r != 0.0f) {
+                        u = rintf(target / r);
+                        if (u < 1.0f) u = 1.0f;
+                        if (u > 255.0f) u = 255.0f;
+                    }
+                    stored = (uint16_t)u;
+                    d = r * u;
+                } else {
+                    stored = bf16_rne_bits(target);
+                    d = bf16_float(stored);
+                }
+                for (int64_t k = 0; k < gw; ++k) qc[k] = wq_code(wg[k], d);
+                double err = wq_sq_err(wg, qc, d, gw);
+                if (best < 0 || err < best_err) {
+                    best = c;
+                    best_err = err;
+                    best_scale = stored;
+                }
+            }
+            /* the winner's codes, recomputed from its scale */
+            float d = (fmt == ORC_FMT_U8G256_BF16ROW) ? r * (float)best_scale : bf16_float(best_scale);
+            for (int64_t k = 0; k < gw; ++k) out[k] = wq_code(wg[k], d);
+            if (fmt == ORC_FMT_U8G256_BF16ROW)
+                ((uint8_t *)gscale)[n * G + g] = (uint8_t)best_scale;
+            else
+                ((uint16_t *)gscale)[n * G + g] = best_scale;
+        }
+        free(wr);
+        free(qc);
+    }
     return status;
 }

@@ -117,3 +117,20 @@ def make(M: int, K: int, N: int, fmt: int = FMT_U8G256_BF16ROW, seed: int = 0,
 def make_workload(name: str, seed: int = 0) -> Inputs:
     w = WORKLOADS[name]
     return make(w.M, w.K, w.N, w.fmt, seed)
+
+
+def make_float_weights(N: int, K: int, seed: int = 0, std: float = 0.02,
+                       outlier_frac: float = 0.005, outlier_mul: float = 8.0) -> np.ndarray:
+    """Synthetic float weights for the weight-side quantiser, f32 [N][K].
+
+    Draw order, one ``numpy.random.Generator(PCG64(seed))``:
+    1. W = standard_normal((N, K), float32) * std
+    2. mask = random((N, K)) < outlier_frac; W[mask] *= outlier_mul
+    """
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(std)
+    mask = rng.random((N, K)) < outlier_frac
+    W[mask] *= np.float32(outlier_mul)
+    return W

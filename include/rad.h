@@ -69,6 +69,8 @@ enum rad_format {
 #define RAD_QUANT_MAX_K 65536
 /* Largest M that rad_w8a8_gemv accepts. */
 #define RAD_GEMV_MAX_M 128
+/* Largest K that rad_quant_weight_i8 accepts (a rotated row is held on chip). */
+#define RAD_QUANT_WEIGHT_MAX_K 32768
 
 /*
  * A quantised weight in the rotated domain.  Codes are int8 in -127..127 and
@@ -180,6 +182,44 @@ int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w,
  */
 int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weight *w, float *y,
                     int64_t M, rad_stream_t stream);
+
+/*
+ * rad_quant_weight_i8 -- quantise float weights into either format above:
+ * rotate, then round to nearest with a scale searched per group for least
+ * error (model card "Qwen3.8-Flash-Next, IQR-V4 -- radiance container",
+ * section "How this file was made": recipe rules with int8 codes, group 128,
+ * bf16 scale, fwht128 transform, clamp=sym, rule=search, and table row
+ * "Trunk": a scale per 128 columns searched for least error; model card
+ * "Qwen3.8-27B IQ8R + DFlash2 -- radiance container", same section: int8
+ * codes, group 256, u8 scale under a bf16 scale per row, clamp=sym,
+ * rule=search.  Those cards then fit the codes by GPTQ, which needs
+ * calibration Hessians; this call is the round-to-nearest form.)
+ *
+ *   W       f32 [N][K] weights (unrotated), 16-byte aligned.
+ *   codes   int8 [N][K] output, 16-byte aligned.
+ *   gscale  output: uint8 [N][K/256] (RAD_FMT_U8G256_BF16ROW) or bf16 bits
+ *           [N][K/128] (RAD_FMT_BF16G128), 4-byte aligned.
+ *   rscale  output bf16 bits [N] for RAD_FMT_U8G256_BF16ROW (4-byte aligned);
+ *           must be NULL for RAD_FMT_BF16G128.
+ *   N >= 0; K > 0, K % group width == 0, K <= RAD_QUANT_WEIGHT_MAX_K.
+ *
+ * Per row: w~ = W rotated as by rad_fwht128 (bit-identical).  Per group g with
+ * amax = max |w~| over the group, candidate c = 0..15 aims at the scale
+ * t_c = (amax * (64 - c) / 64) / 127 (f32 product, then f32 division):
+ *   RAD_FMT_BF16G128: stored b = bf16(t_c) (nearest, ties to even), d = b;
+ *   RAD_FMT_U8G256_BF16ROW: r = bf16((amax_row / 127) / 255) with amax_row
+ *     = max |w~| over the row, stored u8 = clamp(rne(t_c / r), 1, 255),
+ *     d = r * u8 (r = 0, an all-zero row, stores u8 = 1 and zero codes).
+ * Codes are clamp(rne(w~ / d), -127, 127) (f32 division; d = 0 gives 0).  The
+ * candidate with the least f64 sum of (w~ - d * code)^2 over the group wins
+ * (the sum taken as a balanced pairwise tree in index order; ties go to the
+ * smaller c).  The result is deterministic and bit-identical across calls.
+ * The outputs feed rad_w8a8_gemv / rad_w8a8_gemm directly.  No output may
+ * overlap W or another output (RAD_E_ALIAS).  Non-finite weights give
+ * unspecified results.
+ */
+int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
+                        int64_t K, int32_t fmt, rad_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rad_strerror(int status);

@@ -30,9 +30,10 @@ RAD_FMT_BF16G128 = 1
 GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128}
 RAD_QUANT_MAX_K = 65536
 RAD_GEMV_MAX_M = 128
+RAD_QUANT_WEIGHT_MAX_K = 32768
 
 EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
-           "rad_strerror")
+           "rad_quant_weight_i8", "rad_strerror")
 
 
 class RadError(RuntimeError):
@@ -69,8 +70,9 @@ def lib() -> ctypes.CDLL:
         L.rad_w8a8_gemv.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
         L.rad_w8a8_gemm.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
         L.rad_w8a8_linear.argtypes = [vp, vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp]
+        L.rad_quant_weight_i8.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int32, vp]
         for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm,
-                  L.rad_w8a8_linear):
+                  L.rad_w8a8_linear, L.rad_quant_weight_i8):
             f.restype = ci
         L.rad_strerror.argtypes = [ci]
         L.rad_strerror.restype = ctypes.c_char_p
@@ -226,3 +228,27 @@ def linear(x, w: W8A8Weight, q=None, scale=None, y=None):
     _check(lib().rad_w8a8_linear(x.data_ptr(), q.data_ptr(), scale.data_ptr(), ctypes.byref(d),
                                  y.data_ptr(), M, _stream(x)), "rad_w8a8_linear")
     return y, q, scale
+
+
+def quant_weight_i8(W, fmt: int, codes=None, gscale=None, rscale=None) -> W8A8Weight:
+    """Rotate and quantise f32 weights ``W`` [N][K] into format ``fmt``."""
+    torch = _torch()
+    _dev(W, torch.float32, "W")
+    N, K = W.shape
+    G = K // GROUP_WIDTH[fmt]
+    if codes is None:
+        codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if gscale is None:
+        gdt = torch.uint8 if fmt == RAD_FMT_U8G256_BF16ROW else torch.int16
+        gscale = torch.empty((N, G), dtype=gdt, device=W.device)
+    if rscale is None and fmt == RAD_FMT_U8G256_BF16ROW:
+        rscale = torch.empty((N,), dtype=torch.int16, device=W.device)
+    _dev(codes, torch.int8, "codes")
+    if not (gscale.is_cuda and gscale.is_contiguous()):
+        raise TypeError("gscale must be a contiguous GPU tensor")
+    if rscale is not None and not (rscale.is_cuda and rscale.is_contiguous()):
+        raise TypeError("rscale must be a contiguous GPU tensor")
+    _check(lib().rad_quant_weight_i8(W.data_ptr(), codes.data_ptr(), gscale.data_ptr(),
+                                     None if rscale is None else rscale.data_ptr(), N, K, fmt,
+                                     _stream(W)), "rad_quant_weight_i8")
+    return W8A8Weight(codes, gscale, rscale, fmt)

@@ -1,0 +1,205 @@
+// quant_weight.hip -- weight-side int8 quantiser: rotate each 128-block of a
+// float weight row, then choose, per K group, the scale with the least
+// squared error among a fixed set of clipping candidates (gfx950).
+//
+// What is computed (recipe rules of section "How this file was made" on the
+// model cards "Qwen3.8-Flash-Next, IQR-V4 -- radiance container": int8
+// codes, group 128, bf16 scale, fwht128 transform, symmetric clamp, scale
+// searched for least error; and "Qwen3.8-27B IQ8R + DFlash2 -- radiance
+// container": int8 codes, group 256, u8 scale under a bf16 scale per row):
+//
+//   w~ = the row rotated per 128-block (same butterfly network and bits as
+//        the activation rotation);
+//   candidates c = 0..15 of a group: target_c = (amax_g * (64 - c) / 64) / 127
+//        (f32 product, then f32 division);
+//   head format: stored scale bf16_rne(target_c), d = its value;
+//   u8 format:   row scale r = bf16_rne((amax_row / 127) / 255), stored
+//        u8 = clamp(rne(target_c / r), 1, 255), d = r * u8 (exact);
+//   codes clamp(rne(w~ / d), -127, 127) (f32 division; d = 0 gives 0);
+//   error: sum over the group of (w~ - d q)^2 in f64, the sum taken as the
+//        balanced pairwise tree over the group in index order;
+//   the least error wins, ties to the smaller c.
+//
+// Layout: one 256-thread workgroup per weight row.  Phase 1 rotates the row
+// block by block (16 lanes per block, butterflies in registers and DPP) into
+// LDS and records each block's largest magnitude.  Phase 2 gives every wave
+// whole groups: lane i of a wave holds the 4 consecutive elements 4i..4i+3 of
+// a 256-element span (one u8 group, or two head groups on the two half-waves),
+// so the pairwise error tree is the lane's own 2 levels followed by
+// xor-butterflies across lanes: each level adds a lane's partial and its
+// partner's, which is the tree's left + right on the lower lane and the same
+// sum (IEEE addition commutes) on the upper one.  All f64 arithmetic uses
+// explicitly rounded operations, so no multiply-add is contracted.
+#include "rad_device.h"
+#include "rad_launch.h"
+#include "rotate_quant.h"
+
+namespace rad {
+namespace {
+
+constexpr int kFmtU8 = 0;
+constexpr int kWqCandidates = 16;
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float wq_code(float w, float d) {
+    if (d == 0.0f) return 0.0f;
+    const float r = __builtin_rintf(w / d);
+    return fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
+// (w - d q)^2 in f64; d q is exact in f32 (at most 16 + 7 significant bits)
+// and the difference is exact in f64.
+__device__ __forceinline__ double wq_sq(float w, float d, float q) {
+    const double e = __dsub_rn(static_cast<double>(w), static_cast<double>(d * q));
+    return __dmul_rn(e, e);
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int x) {
+    const int lo = __double2loint(v), hi = __double2hiint(v);
+    return __hiloint2double(__shfl_xor(hi, x), __shfl_xor(lo, x));
+}
+
+// Pairwise tree over the lanes of a span of 2^levels lanes (levels = 6 for a
+// whole wave, 5 for a half wave).
+template <int LEVELS>
+__device__ __forceinline__ double tree_sum(double v) {
+#pragma unroll
+    for (int l = 0; l < LEVELS; ++l) v = __dadd_rn(v, shfl_xor_f64(v, 1 << l));
+    return v;
+}
+
+template <int FMT, int KMAX>
+__global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restrict__ W,
+                                                           int8_t *__restrict__ codes,
+                                                           void *__restrict__ gscale,
+                                                           uint16_t *__restrict__ rscale, int K) {
+    constexpr int GW = (FMT == kFmtU8) ? 256 : 128;
+    constexpr int LEVELS = (FMT == kFmtU8) ? 6 : 5;       // lanes per group = 2^LEVELS
+    __shared__ __attribute__((aligned(16))) float wt[KMAX];
+    __shared__ float bamax[KMAX / 128];
+
+    const int n = blockIdx.x;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int l16 = lane & 15, r4 = lane >> 4;
+    const int nblk = K / 128;
+    const float *wrow = W + static_cast<int64_t>(n) * K;
+
+    // ---- phase 1: rotate every 128-block into LDS, block amax
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+        const int blk = b0 + wid * 4 + r4;
+        if (blk < nblk) {
+            Blk8 v;
+            v.lo = *reinterpret_cast<const float4 *>(wrow + blk * 128 + 4 * l16);
+            v.hi = *reinterpret_cast<const float4 *>(wrow + blk * 128 + 64 + 4 * l16);
+            fwht128_regs(v, l16);
+            *reinterpret_cast<float4 *>(&wt[blk * 128 + 4 * l16]) = v.lo;
+            *reinterpret_cast<float4 *>(&wt[blk * 128 + 64 + 4 * l16]) = v.hi;
+            float a = fmaxf(amax4(v.lo), amax4(v.hi));
+            a = fmaxf(a, lane_xor<1>(a));
+            a = fmaxf(a, lane_xor<2>(a));
+            a = fmaxf(a, lane_xor<4>(a));
+            a = fmaxf(a, lane_xor<8>(a));
+            if (l16 == 0) bamax[blk] = a;
+        }
+    }
+    __syncthreads();
+
+    // ---- row scale (u8 format), computed by every wave alike
+    float rv = 0.0f;
+    if constexpr (FMT == kFmtU8) {
+        float a = 0.0f;
+        for (int j = lane; j < nblk; j += 64) a = fmaxf(a, bamax[j]);
+        const float amax_row = wave_max_f32(a);
+        const uint16_t rb = bf16_rne((amax_row / 127.0f) / 255.0f);
+        rv = bf16_to_f32(rb);
+        if (threadIdx.x == 0) rscale[n] = rb;
+    }
+
+    // ---- phase 2: one 256-element span per wave at a time
+    const int G = K / GW;
+    // head format with an odd group count: the last span holds one group; its
+    // upper half-wave reads LDS words past K (still inside wt) and stores nothing
+    const int nspan = (K + 255) / 256;
+    const int half = lane >> 5;                        // head format: which group of the span
+    for (int sp = wid; sp < nspan; sp += 4) {
+        const float4 w = *reinterpret_cast<const float4 *>(&wt[sp * 256 + 4 * lane]);
+        float amax;
+        int g;
+        if constexpr (FMT == kFmtU8) {
+            g = sp;
+            amax = fmaxf(bamax[2 * sp], bamax[2 * sp + 1]);
+        } else {
+            g = 2 * sp + half;
+            amax = bamax[g];
+        }
+        float best_d = 0.0f;
+        uint32_t best_stored = 0;
+        double best_err = 0.0;
+#pragma unroll 1
+        for (int c = 0; c < kWqCandidates; ++c) {
+            const float target = (amax * (static_cast<float>(64 - c) / 64.0f)) / 127.0f;
+            float d;
+            uint32_t stored;
+            if constexpr (FMT == kFmtU8) {
+                float u = 1.0f;
+                if (rv != 0.0f) u = fminf(fmaxf(__builtin_rintf(target / rv), 1.0f), 255.0f);
+                stored = static_cast<uint32_t>(u);
+                d = rv * u;
+            } else {
+                stored = bf16_rne(target);
+                d = bf16_to_f32(static_cast<uint16_t>(stored));
+            }
+            const double s01 = __dadd_rn(wq_sq(w.x, d, wq_code(w.x, d)), wq_sq(w.y, d, wq_code(w.y, d)));
+            const double s23 = __dadd_rn(wq_sq(w.z, d, wq_code(w.z, d)), wq_sq(w.w, d, wq_code(w.w, d)));
+            const double err = tree_sum<LEVELS>(__dadd_rn(s01, s23));
+            if (c == 0 || err < best_err) {
+                best_err = err;
+                best_d = d;
+                best_stored = stored;
+            }
+        }
+        const uint32_t b0 = static_cast<uint32_t>(static_cast<int>(wq_code(w.x, best_d))) & 0xFFu;
+        const uint32_t b1 = static_cast<uint32_t>(static_cast<int>(wq_code(w.y, best_d))) & 0xFFu;
+        const uint32_t b2 = static_cast<uint32_t>(static_cast<int>(wq_code(w.z, best_d))) & 0xFFu;
+        const uint32_t b3 = static_cast<uint32_t>(static_cast<int>(wq_code(w.w, best_d))) & 0xFFu;
+        if (g < G) {
+            *reinterpret_cast<uint32_t *>(codes + static_cast<int64_t>(n) * K + sp * 256 + 4 * lane) =
+                b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+            if constexpr (FMT == kFmtU8) {
+                if (lane == 0) static_cast<uint8_t *>(gscale)[static_cast<int64_t>(n) * G + g] = static_cast<uint8_t>(best_stored);
+            } else {
+                if ((lane & 31) == 0)
+                    static_cast<uint16_t *>(gscale)[static_cast<int64_t>(n) * G + g] = static_cast<uint16_t>(best_stored);
+            }
+        }
+    }
+}
+
+template <int FMT, int KMAX>
+hipError_t launch_qw(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
+                     int64_t K, hipStream_t st) {
+    hipLaunchKernelGGL((quant_weight_kernel<FMT, KMAX>), dim3(static_cast<uint32_t>(N)), dim3(256), 0,
+                       st, W, codes, gscale, rscale, static_cast<int>(K));
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_qw_fmt(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
+                         int64_t K, hipStream_t st) {
+    if (K <= 8192) return launch_qw<FMT, 8192>(W, codes, gscale, rscale, N, K, st);
+    return launch_qw<FMT, kQuantWeightMaxK>(W, codes, gscale, rscale, N, K, st);
+}
+
+}  // namespace
+
+hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
+                               int64_t N, int64_t K, int fmt, hipStream_t st) {
+    return fmt == kFmtU8 ? launch_qw_fmt<0>(W, codes, gscale, rscale, N, K, st)
+                         : launch_qw_fmt<1>(W, codes, gscale, rscale, N, K, st);
+}
+
+}  // namespace rad

@@ -23,6 +23,7 @@ Span span(const void *p, int64_t bytes) {
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 constexpr int64_t kI32Max = 2147483647;
+static_assert(RAD_QUANT_WEIGHT_MAX_K == rad::kQuantWeightMaxK, "header and kernel agree on the largest K");
 
 int group_width(int32_t fmt) {
     if (fmt == RAD_FMT_U8G256_BF16ROW) return 256;
@@ -135,6 +136,28 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
     e = (M <= RAD_GEMV_MAX_M) ? rad::launch_gemv(q, scale, wa, y, M, nullptr, st)
                               : rad::launch_gemm(q, scale, wa, y, M, nullptr, st);
     return hip_status(e);
+}
+
+int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
+                        int64_t K, int32_t fmt, rad_stream_t stream) {
+    const int gw = group_width(fmt);
+    if (gw == 0) return RAD_E_FMT;
+    if (fmt == RAD_FMT_U8G256_BF16ROW && !rscale) return RAD_E_FMT;
+    if (fmt == RAD_FMT_BF16G128 && rscale) return RAD_E_FMT;
+    if (N < 0 || K <= 0 || K % 128 != 0 || K % gw != 0) return RAD_E_SHAPE;
+    if (K > RAD_QUANT_WEIGHT_MAX_K || N > kI32Max) return RAD_E_RANGE;
+    if (N == 0) return RAD_OK;
+    if (!W || !codes || !gscale) return RAD_E_NULL;
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(gscale, 4) || (rscale && !aligned(rscale, 4)))
+        return RAD_E_ALIGN;
+    const int esz = (fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
+    const Span ws = span(W, N * K * 4), cs = span(codes, N * K), gs = span(gscale, N * (K / gw) * esz),
+               rs = rscale ? span(rscale, N * 2) : Span{0, 0};
+    if (overlap(ws, cs) || overlap(ws, gs) || overlap(ws, rs) || overlap(cs, gs) || overlap(cs, rs) ||
+        overlap(gs, rs))
+        return RAD_E_ALIAS;
+    return hip_status(rad::launch_quant_weight(W, codes, gscale, rscale, N, K, fmt,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 const char *rad_strerror(int status) {

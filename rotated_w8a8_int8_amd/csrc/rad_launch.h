@@ -25,6 +25,10 @@ hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, flo
 bool fused_decode_supported(const WeightArgs &w, int64_t M);
 hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
                                hipStream_t st);
+// Weight-side quantiser; K <= kQuantWeightMaxK.
+constexpr int kQuantWeightMaxK = 32768;
+hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
+                               int64_t N, int64_t K, int fmt, hipStream_t st);
 hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st);
 

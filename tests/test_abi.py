@@ -46,7 +46,7 @@ def test_constants_match_header():
                  "RAD_FMT_BF16G128"):
         m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, h)
         assert m and int(m.group(1)) == getattr(B, name), name
-    for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M"):
+    for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M", "RAD_QUANT_WEIGHT_MAX_K"):
         m = re.search(r"#define %s (\d+)" % name, h)
         assert m and int(m.group(1)) == getattr(B, name)
 
@@ -150,3 +150,29 @@ def test_linear_entry_validation():
     assert call(desc(), q=Bp + 0x100000 + 64) == B.RAD_E_ALIAS      # codes out over x
     assert call(desc(), s=D) == B.RAD_E_ALIAS                       # scales out over gscale
     assert call(desc(), y=Bp + 0x100000) == B.RAD_E_ALIAS           # y over x
+
+
+# -------------------------------------------------------- weight quantiser --
+
+def test_quant_weight_validation():
+    f = B.lib().rad_quant_weight_i8
+    U8, HEAD = B.RAD_FMT_U8G256_BF16ROW, B.RAD_FMT_BF16G128
+    assert f(A, Bp, C, D, 4, 512, 7, None) == B.RAD_E_FMT
+    assert f(A, Bp, C, None, 4, 512, U8, None) == B.RAD_E_FMT        # u8 needs row scales
+    assert f(A, Bp, C, D, 4, 512, HEAD, None) == B.RAD_E_FMT         # head forbids them
+    assert f(A, Bp, C, D, 4, 384, U8, None) == B.RAD_E_SHAPE         # K % 256
+    assert f(A, Bp, C, None, 4, 200, HEAD, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, C, D, -1, 512, U8, None) == B.RAD_E_SHAPE
+    assert f(A, Bp, C, D, 4, B.RAD_QUANT_WEIGHT_MAX_K + 256, U8, None) == B.RAD_E_RANGE
+    assert f(A, Bp, C, D, 1 << 31, 512, U8, None) == B.RAD_E_RANGE
+    assert f(None, None, None, D, 0, 512, U8, None) == B.RAD_OK       # empty
+    assert f(None, Bp, C, D, 4, 512, U8, None) == B.RAD_E_NULL
+    assert f(A, None, C, D, 4, 512, U8, None) == B.RAD_E_NULL
+    assert f(A, Bp, None, D, 4, 512, U8, None) == B.RAD_E_NULL
+    assert f(A + 4, Bp, C, D, 4, 512, U8, None) == B.RAD_E_ALIGN
+    assert f(A, Bp + 8, C, D, 4, 512, U8, None) == B.RAD_E_ALIGN
+    assert f(A, Bp, C + 2, D, 4, 512, U8, None) == B.RAD_E_ALIGN
+    assert f(A, Bp, C, D + 2, 4, 512, U8, None) == B.RAD_E_ALIGN
+    assert f(A, A + 4096, C, D, 4, 512, U8, None) == B.RAD_E_ALIAS   # codes inside W
+    assert f(A, Bp, Bp + 512, D, 4, 512, U8, None) == B.RAD_E_ALIAS  # scales inside codes
+    assert f(A, Bp, C, C + 4, 4, 512, U8, None) == B.RAD_E_ALIAS     # row scales over group scales

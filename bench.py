@@ -2,6 +2,7 @@
 """Benchmark of the rotated W8A8 int8 linear layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
+    python bench.py --op quant_weight [--workload NAME]
 
 A step is one pass of the whole layer over one batch of synthetic input that
 is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
@@ -20,6 +21,15 @@ once) per second for M <= 128, or 2*M*N*K int8 operations per second for
 larger M.  `roofline` is the dominant kernel timed alone with HIP events on
 its own stream, against MI355X's published peak.  `cpu_baseline` is the CPU
 oracle on a bounded sample of the same workload.
+
+--op quant_weight times rad_quant_weight_i8 instead: quantising synthetic f32
+weights of the named workload's weight shape and format (one launch per
+step).  Its `value` is algorithmic bytes per second (f32 weights in, codes and
+scales out); the kernel is bound by its scale search on the vector ALUs, so
+`roofline` counts 8 operations per (weight, candidate scale) evaluation
+(multiply by the reciprocal, round, two clamps, scale times code, subtract,
+square, accumulate) against the vector ALU peak without packed FP32 math:
+256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations per second.
 """
 from __future__ import annotations
 
@@ -37,6 +47,9 @@ METRIC = "W8A8 rotated linear: HBM GB/s (M≤128) and int8 TOPS (M=8192), % of r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 COPY_TARGET_BYTES = 1 << 30    # distinct weight bytes rotated through per round
+VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed f32 lane-operations, 39.3 T/s
+WQ_CANDIDATES = 16             # scale candidates per group of rad_quant_weight_i8
+WQ_OPS_PER_EVAL = 8            # operations per (weight, candidate) evaluation
 
 
 def parse():
@@ -45,6 +58,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_gate_up")
+    ap.add_argument("--op", choices=("linear", "quant_weight"), default="linear",
+                    help="linear: the whole layer (default); quant_weight: the weight-side "
+                         "quantiser on the workload's weight shape")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -77,22 +93,31 @@ def sizes(wl):
     )
 
 
-def kernel_source_hash():
+def kernel_sources(wl):
+    """The source files the dominant kernel of a workload's step is built from."""
+    common = ["rad_device.h", "rad_launch.h"]
+    if wl.M == 1:
+        return ["gemv.hip", "rotate_quant.h"] + common       # the fused one-token kernel
+    if wl.M <= 128:
+        return ["gemv.hip"] + common
+    return ["gemm.hip"] + common
+
+
+def kernel_source_hash(wl):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rotated_w8a8_int8_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in sorted(kernel_sources(wl)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload):
-    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernels."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+def load_traffic(wl):
+    """HBM bytes per launch from rocprofv3 counters, if taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(wl):
         return None
     return rec.get("bytes_per_launch")
 
@@ -157,7 +182,8 @@ def traffic_from(args):
         "write_bytes_per_launch": int(round(wbytes)),
         "algorithmic_bytes_per_launch": alg,
         "traffic_over_algorithmic": round((fbytes + wbytes) / alg, 4),
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_sources": kernel_sources(wl),
+        "kernel_source_sha256_16": kernel_source_hash(wl),
     }
     out = os.path.join(ROOT, "profiles", "traffic_%s.json" % wl.name)
     with open(out, "w") as fh:
@@ -189,6 +215,9 @@ def main():
     B.lib()                                            # fail loudly if not built
 
     wl = W.WORKLOADS[args.workload]
+    if args.op == "quant_weight":
+        bench_quant_weight(args, wl)
+        return
     sz = sizes(wl)
     big = wl.M > B.RAD_GEMV_MAX_M
     steps = args.steps if args.steps is not None else (20 if big else 3000)
@@ -291,7 +320,7 @@ def main():
     roof["kernel"] = kname
     roof["bytes_per_launch"] = kbytes
     roof["us_per_launch"] = round(ms_k * 1e3, 3)
-    roof["traffic"] = load_traffic(wl.name)
+    roof["traffic"] = load_traffic(wl)
 
     # ---- parity of the timed buffers against the oracle (sampled rows)
     import oracle
@@ -350,6 +379,93 @@ def main():
         "parity_on_timed_buffers": parity,
     }
     print(json.dumps(out))
+
+
+def bench_quant_weight(args, wl):
+    """rad_quant_weight_i8 on f32 weights of the workload's weight shape."""
+    import torch
+    import oracle
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
+    N, K, fmt = wl.N, wl.K, wl.fmt
+    G = wl.G
+    esz = 1 if fmt == W.FMT_U8G256_BF16ROW else 2
+    alg = N * K * 4 + N * K + N * G * esz + (N * 2 if fmt == W.FMT_U8G256_BF16ROW else 0)
+    steps = args.steps if args.steps is not None else 20
+    warmup = args.warmup if args.warmup is not None else 3
+    Wf = W.make_float_weights(N, K, seed=0)
+    dev = torch.device("cuda", 0)
+    Wd = torch.from_numpy(Wf).to(dev)
+    out = B.quant_weight_i8(Wd, fmt)
+    stream = torch.cuda.Stream(device=dev)             # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            B.quant_weight_i8(Wd, fmt, out.codes, out.gscale, out.rscale)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            B.quant_weight_i8(Wd, fmt, out.codes, out.gscale, out.rscale)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / steps
+    value = alg / (ms * 1e-3) / 1e9
+    tops = N * K * WQ_CANDIDATES * WQ_OPS_PER_EVAL / (ms * 1e-3) / 1e12
+    roof = {"bound": "alu", "achieved": round(tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+            "unit": "T lane-ops/s", "frac": round(tops / VALU_PEAK_TOPS, 4), "traffic": None,
+            "kernel": "rad_quant_weight_i8", "bytes_per_launch": alg, "us_per_launch": round(ms * 1e3, 3),
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4)}
+
+    # parity of the timed outputs against the oracle on sampled rows
+    rows = np.unique(np.linspace(0, N - 1, 8).astype(int))
+    co, go, ro = oracle.quant_weight_i8(Wf[rows], fmt)
+    gs = out.gscale.cpu().numpy()
+    if fmt != W.FMT_U8G256_BF16ROW:
+        gs = gs.view(np.uint16)
+    parity = bool(np.array_equal(out.codes.cpu().numpy()[rows], co) and np.array_equal(gs[rows], go))
+    if ro is not None:
+        parity = parity and bool(np.array_equal(out.rscale.cpu().numpy().view(np.uint16)[rows], ro))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nrow = min(N, 256)
+        sample = np.ascontiguousarray(Wf[:nrow])
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            oracle.quant_weight_i8(sample, fmt)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - c0) / n
+        cpu = {"value": round(alg * nrow / N / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": "%d of %d weight rows, %d repetitions, %.1f s"
+                                           % (nrow, N, n, dt * n)}
+    print(json.dumps({
+        "metric": "weight-side rotated int8 quantiser: GB/s (f32 weights in, codes and scales out)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "quant_weight_" + wl.name, "N": N, "K": K,
+                   "format": "u8g256_bf16row" if fmt == W.FMT_U8G256_BF16ROW else "bf16g128",
+                   "launch": "eager", "host_ms_per_step": round((t1 - t0) * 1e3 / steps, 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_on_timed_buffers": parity,
+    }))
 
 
 if __name__ == "__main__":

@@ -51,6 +51,18 @@ __device__ __forceinline__ float wq_code(float w, float d) {
     return fminf(fmaxf(r, -127.0f), 127.0f);
 }
 
+// The same code through the reciprocal: t = w * fl(1/d) is within
+// 1.5 * 2^-23 |w / d| of the rounded quotient fl(w / d), so both round to the
+// same integer (and clamp alike) unless t lies within 2^-13 of a half-integer
+// (|t| < 256 there; larger |t| clamps either way).  `near` flags that case;
+// the caller then redoes the element with the division.  Valid for d in the
+// normal range [2^-120, 2^120], where 1/d is finite and normal.
+__device__ __forceinline__ float wq_code_rcp(float w, float rd, bool &near) {
+    const float t = w * rd;
+    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
+    return fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+}
+
 // (w - d q)^2 in f64; d q is exact in f32 (at most 16 + 7 significant bits)
 // and the difference is exact in f64.
 __device__ __forceinline__ double wq_sq(float w, float d, float q) {
@@ -58,29 +70,41 @@ __device__ __forceinline__ double wq_sq(float w, float d, float q) {
     return __dmul_rn(e, e);
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double v, int x) {
+// The f64 held by lane (lane ^ X): DPP inside a 16-lane row, else a permute.
+template <int X>
+__device__ __forceinline__ double xor_f64(double v) {
     const int lo = __double2loint(v), hi = __double2hiint(v);
-    return __hiloint2double(__shfl_xor(hi, x), __shfl_xor(lo, x));
+    if constexpr (X < 16) return __hiloint2double(lane_xor<X>(hi), lane_xor<X>(lo));
+    else return __hiloint2double(__shfl_xor(hi, X), __shfl_xor(lo, X));
 }
 
-// Pairwise tree over the lanes of a span of 2^levels lanes (levels = 6 for a
-// whole wave, 5 for a half wave).
+// Pairwise tree over the lanes of a span of 2^LEVELS lanes (6: a whole wave,
+// 5: a half wave).
 template <int LEVELS>
 __device__ __forceinline__ double tree_sum(double v) {
-#pragma unroll
-    for (int l = 0; l < LEVELS; ++l) v = __dadd_rn(v, shfl_xor_f64(v, 1 << l));
+    v = __dadd_rn(v, xor_f64<1>(v));
+    v = __dadd_rn(v, xor_f64<2>(v));
+    v = __dadd_rn(v, xor_f64<4>(v));
+    v = __dadd_rn(v, xor_f64<8>(v));
+    v = __dadd_rn(v, xor_f64<16>(v));
+    if constexpr (LEVELS == 6) v = __dadd_rn(v, xor_f64<32>(v));
     return v;
 }
 
-template <int FMT, int KMAX>
+// LDS: the rotated row (K floats, plus 128 so that the last span of an odd
+// head-group count stays inside), then one amax per 128-block.
+inline size_t quant_weight_lds_bytes(int64_t K) { return static_cast<size_t>(K + 128 + K / 128) * 4; }
+
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restrict__ W,
                                                            int8_t *__restrict__ codes,
                                                            void *__restrict__ gscale,
                                                            uint16_t *__restrict__ rscale, int K) {
     constexpr int GW = (FMT == kFmtU8) ? 256 : 128;
     constexpr int LEVELS = (FMT == kFmtU8) ? 6 : 5;       // lanes per group = 2^LEVELS
-    __shared__ __attribute__((aligned(16))) float wt[KMAX];
-    __shared__ float bamax[KMAX / 128];
+    extern __shared__ __attribute__((aligned(16))) float qw_lds[];
+    float *wt = qw_lds;
+    float *bamax = qw_lds + K + 128;
 
     const int n = blockIdx.x;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -122,7 +146,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
     // ---- phase 2: one 256-element span per wave at a time
     const int G = K / GW;
     // head format with an odd group count: the last span holds one group; its
-    // upper half-wave reads LDS words past K (still inside wt) and stores nothing
+    // upper half-wave reads the 128 spare LDS words past K and stores nothing
     const int nspan = (K + 255) / 256;
     const int half = lane >> 5;                        // head format: which group of the span
     for (int sp = wid; sp < nspan; sp += 4) {
@@ -134,7 +158,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
             amax = fmaxf(bamax[2 * sp], bamax[2 * sp + 1]);
         } else {
             g = 2 * sp + half;
-            amax = bamax[g];
+            amax = g < G ? bamax[g] : 0.0f;
         }
         float best_d = 0.0f;
         uint32_t best_stored = 0;
@@ -153,8 +177,23 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
                 stored = bf16_rne(target);
                 d = bf16_to_f32(static_cast<uint16_t>(stored));
             }
-            const double s01 = __dadd_rn(wq_sq(w.x, d, wq_code(w.x, d)), wq_sq(w.y, d, wq_code(w.y, d)));
-            const double s23 = __dadd_rn(wq_sq(w.z, d, wq_code(w.z, d)), wq_sq(w.w, d, wq_code(w.w, d)));
+            // codes: through the reciprocal where that provably rounds alike,
+            // else (any lane of the wave near a half-integer, or d outside
+            // the normal range) through the division for the whole wave
+            bool near = !(d >= 0x1p-120f && d <= 0x1p120f);
+            const float rd = 1.0f / d;
+            float q0 = wq_code_rcp(w.x, rd, near);
+            float q1 = wq_code_rcp(w.y, rd, near);
+            float q2 = wq_code_rcp(w.z, rd, near);
+            float q3 = wq_code_rcp(w.w, rd, near);
+            if (__any(near)) {
+                q0 = wq_code(w.x, d);
+                q1 = wq_code(w.y, d);
+                q2 = wq_code(w.z, d);
+                q3 = wq_code(w.w, d);
+            }
+            const double s01 = __dadd_rn(wq_sq(w.x, d, q0), wq_sq(w.y, d, q1));
+            const double s23 = __dadd_rn(wq_sq(w.z, d, q2), wq_sq(w.w, d, q3));
             const double err = tree_sum<LEVELS>(__dadd_rn(s01, s23));
             if (c == 0 || err < best_err) {
                 best_err = err;
@@ -179,27 +218,26 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
     }
 }
 
-template <int FMT, int KMAX>
+template <int FMT>
 hipError_t launch_qw(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
                      int64_t K, hipStream_t st) {
-    hipLaunchKernelGGL((quant_weight_kernel<FMT, KMAX>), dim3(static_cast<uint32_t>(N)), dim3(256), 0,
-                       st, W, codes, gscale, rscale, static_cast<int>(K));
+    const size_t lds = quant_weight_lds_bytes(K);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&quant_weight_kernel<FMT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(quant_weight_kernel<FMT>, dim3(static_cast<uint32_t>(N)), dim3(256), lds, st, W,
+                       codes, gscale, rscale, static_cast<int>(K));
     return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_qw_fmt(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
-                         int64_t K, hipStream_t st) {
-    if (K <= 8192) return launch_qw<FMT, 8192>(W, codes, gscale, rscale, N, K, st);
-    return launch_qw<FMT, kQuantWeightMaxK>(W, codes, gscale, rscale, N, K, st);
 }
 
 }  // namespace
 
 hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
                                int64_t N, int64_t K, int fmt, hipStream_t st) {
-    return fmt == kFmtU8 ? launch_qw_fmt<0>(W, codes, gscale, rscale, N, K, st)
-                         : launch_qw_fmt<1>(W, codes, gscale, rscale, N, K, st);
+    return fmt == kFmtU8 ? launch_qw<0>(W, codes, gscale, rscale, N, K, st)
+                         : launch_qw<1>(W, codes, gscale, rscale, N, K, st);
 }
 
 }  // namespace rad

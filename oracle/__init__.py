@@ -70,8 +70,11 @@ def _load():
         lib.orc_epilogue.argtypes = [p, p, ci, p, p, p, i64, i64, i64]
         lib.orc_linear.argtypes = [p, p, p, ci, p, p, p, i64, i64, i64]
         lib.orc_quant_weight_i8.argtypes = [p, p, p, p, i64, i64, ci]
+        lib.orc_kv_quant_i8.argtypes = [p, p, p, i64, i64]
+        lib.orc_kv_dequant_i8.argtypes = [p, p, p, i64, i64]
         for f in (lib.orc_fwht128, lib.orc_quant_act_i8, lib.orc_group_partials,
-                  lib.orc_epilogue, lib.orc_linear, lib.orc_quant_weight_i8):
+                  lib.orc_epilogue, lib.orc_linear, lib.orc_quant_weight_i8,
+                  lib.orc_kv_quant_i8, lib.orc_kv_dequant_i8):
             f.restype = ci
         _lib = lib
     return _lib
@@ -190,3 +193,24 @@ def quant_weight_i8(W: np.ndarray, fmt: int):
         rscale = None
     _check(_load().orc_quant_weight_i8(_ptr(W), _ptr(codes), _ptr(gscale), _ptr(rscale), N, K, fmt))
     return codes, gscale, rscale
+
+
+def kv_quant_i8(x_bf16: np.ndarray):
+    """int8 KV-cache encode of bf16 rows ``x_bf16`` (uint16 bits) [rows][D]:
+    returns (codes int8 [rows][D], scale f16 bits uint16 [rows])."""
+    x = _c(x_bf16, np.uint16)
+    rows, D = x.shape
+    codes = np.empty((rows, D), np.int8)
+    scale = np.empty((rows,), np.uint16)
+    _check(_load().orc_kv_quant_i8(_ptr(x), _ptr(codes), _ptr(scale), rows, D))
+    return codes, scale
+
+
+def kv_dequant_i8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Read back an int8 KV cache: bf16 bits uint16 [rows][D]."""
+    codes = _c(codes, np.int8)
+    scale = _c(scale, np.uint16)
+    rows, D = codes.shape
+    y = np.empty((rows, D), np.uint16)
+    _check(_load().orc_kv_dequant_i8(_ptr(codes), _ptr(scale), _ptr(y), rows, D))
+    return y

@@ -437,3 +437,90 @@ int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
     }
     return status;
 }
+
+/*
+ * ---- int8 KV-cache codec ----
+ *
+ * Source: model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance container",
+ * section "Serve": with kv-cache-dtype i8 the attention cache is stored as
+ * int8 with one f16 scale per token and head (half of bf16's bytes).
+ * Readings where the card is silent:
+ *   R11 A row is one head's vector of one token, D values, stored as bf16
+ *       (the cache it replaces is bf16).  The scale is f16_rne(amax / 127)
+ *       (f32 division, then rounding to the nearest binary16, ties to even,
+ *       subnormals kept, saturating at the largest finite f16, 65504); codes
+ *       are clamp(rne(x / s), -127, 127) with s the stored f16 value (f32
+ *       division); s = 0 gives zero codes.  No rotation (the card names none
+ *       for the cache).
+ *   R12 Reading back: y = bf16_rne(code * s), the product exact in f32.
+ */
+
+/* f32 -> binary16 bits, round to nearest even, saturating at 65504. */
+static uint16_t f16_rne_bits_sat(float f)
+{
+    union { uint32_t u; float f; } c;
+    c.f = f;
+    uint32_t sign = (c.u >> 16) & 0x8000u;
+    float a = fabsf(f);
+    if (!(a < 65520.0f)) return (uint16_t)(sign | 0x7BFFu);   /* saturate (no inf, no NaN) */
+    if (a >= 0x1p-14f) {
+        /* normal: keep 10 fraction bits of the 23, round half to even */
+        c.f = a;
+        uint32_t e = (c.u >> 23) - 127 + 15;
+        uint32_t m = c.u & 0x7FFFFFu;
+        uint32_t keep = m >> 13, rest = m & 0x1FFFu;
+        if (rest > 0x1000u || (rest == 0x1000u && (keep & 1u))) ++keep;
+        uint32_t bits = (e << 10) + keep;                    /* a carry moves into the exponent */
+        return (uint16_t)(sign | bits);
+    }
+    /* subnormal: value = n * 2^-24, n = rne(a * 2^24) (exact scaling) */
+    float n = rintf(a * 0x1p24f);
+    return (uint16_t)(sign | (uint32_t)n);                   /* n = 1024 is the smallest normal */
+}
+
+static float f16_value(uint16_t h)
+{
+    uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    float v = (e == 0) ? ldexpf((float)m, -24) : ldexpf((float)(m | 0x400u), (int)e - 25);
+    return (h & 0x8000u) ? -v : v;
+}
+
+int orc_kv_quant_i8(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D)
+{
+    if (!x || !codes || !scale || rows < 0 || D <= 0) return ORC_E_ARG;
+    if (fegetround() != FE_TONEAREST) return ORC_E_ROUNDING;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t i = 0; i < D; ++i) {
+            float a = fabsf(bf16_float(x[r * D + i]));
+            if (a > amax) amax = a;
+        }
+        uint16_t sb = f16_rne_bits_sat(amax / 127.0f);
+        scale[r] = sb;
+        float s = f16_value(sb);
+        for (int64_t i = 0; i < D; ++i) {
+            int code = 0;
+            if (s != 0.0f) {
+                float q = rintf(bf16_float(x[r * D + i]) / s);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+                code = (int)q;
+            }
+            codes[r * D + i] = (int8_t)code;
+        }
+    }
+    return ORC_OK;
+}
+
+int orc_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows, int64_t D)
+{
+    if (!codes || !scale || !y || rows < 0 || D <= 0) return ORC_E_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float s = f16_value(scale[r]);
+        for (int64_t i = 0; i < D; ++i)
+            y[r * D + i] = bf16_rne_bits((float)codes[r * D + i] * s);
+    }
+    return ORC_OK;
+}

@@ -134,3 +134,30 @@ def make_float_weights(N: int, K: int, seed: int = 0, std: float = 0.02,
     mask = rng.random((N, K)) < outlier_frac
     W[mask] *= np.float32(outlier_mul)
     return W
+
+
+# int8 KV-cache codec workloads: rows = tokens x KV heads, one head vector
+# (D values) per row.  8 KV heads of 128 (a 27B dense trunk with grouped-query
+# attention) and the 200K-token context the model card serves at.
+KV_WORKLOADS = {
+    "kv_tiny": (3 * 8, 128),
+    "kv_200k": (200000 * 8, 128),
+}
+
+
+def make_kv(rows: int, D: int, seed: int = 0, outlier_frac: float = 0.01,
+            outlier_mul: float = 20.0) -> np.ndarray:
+    """Synthetic bf16 cache rows (uint16 bits) [rows][D].
+
+    Draw order, one ``numpy.random.Generator(PCG64(seed))``:
+    1. v = standard_normal((rows, D), float32)
+    2. mask = random((rows, D)) < outlier_frac; v[mask] *= outlier_mul
+    3. per-row magnitude: v *= exp(uniform(-4, 4, rows))[:, None]
+    then rounded to bf16 (nearest, ties to even).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    v = rng.standard_normal((rows, D), dtype=np.float32)
+    mask = rng.random((rows, D)) < outlier_frac
+    v[mask] *= np.float32(outlier_mul)
+    v *= np.exp(rng.uniform(-4.0, 4.0, size=rows)).astype(np.float32)[:, None]
+    return f32_to_bf16_bits(v)

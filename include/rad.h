@@ -221,6 +221,30 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
 int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *rscale, int64_t N,
                         int64_t K, int32_t fmt, rad_stream_t stream);
 
+/*
+ * rad_kv_quant_i8 / rad_kv_dequant_i8 -- the int8 attention-cache codec
+ * (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance container", section
+ * "Serve": kv-cache-dtype i8 stores the attention cache as int8 with an f16
+ * scale per token and head, half of bf16's bytes).  A row is one head's
+ * vector of one token.
+ *
+ *   x       bf16 bits [rows][D] (encode input; decode output y), 16-byte aligned.
+ *   codes   int8 [rows][D], 8-byte aligned.
+ *   scale   f16 bits [rows], 2-byte aligned.
+ *   rows >= 0; D is 64, 128 or 256 (other head sizes return RAD_E_SHAPE).
+ *
+ * Encode: s = f16(amax / 127) with amax the row's largest |x| (f32 division,
+ * rounded to the nearest f16, ties to even, subnormals kept, saturating at
+ * 65504); codes = clamp(rne(x / s), -127, 127) with s the stored value (f32
+ * division), s = 0 giving zero codes.  Decode: y = bf16(code * s) (the product
+ * is exact in f32; rounded to nearest even).  Outputs may not overlap inputs
+ * or each other (RAD_E_ALIAS).  Non-finite inputs give unspecified results.
+ */
+int rad_kv_quant_i8(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D,
+                    rad_stream_t stream);
+int rad_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows,
+                      int64_t D, rad_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rad_strerror(int status);
 

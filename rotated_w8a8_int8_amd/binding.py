@@ -33,7 +33,8 @@ RAD_GEMV_MAX_M = 128
 RAD_QUANT_WEIGHT_MAX_K = 32768
 
 EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
-           "rad_quant_weight_i8", "rad_strerror")
+           "rad_quant_weight_i8", "rad_kv_quant_i8", "rad_kv_dequant_i8", "rad_strerror")
+KV_HEAD_DIMS = (64, 128, 256)
 
 
 class RadError(RuntimeError):
@@ -71,8 +72,10 @@ def lib() -> ctypes.CDLL:
         L.rad_w8a8_gemm.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, vp]
         L.rad_w8a8_linear.argtypes = [vp, vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp]
         L.rad_quant_weight_i8.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int32, vp]
+        L.rad_kv_quant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.rad_kv_dequant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
         for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm,
-                  L.rad_w8a8_linear, L.rad_quant_weight_i8):
+                  L.rad_w8a8_linear, L.rad_quant_weight_i8, L.rad_kv_quant_i8, L.rad_kv_dequant_i8):
             f.restype = ci
         L.rad_strerror.argtypes = [ci]
         L.rad_strerror.restype = ctypes.c_char_p
@@ -252,3 +255,42 @@ def quant_weight_i8(W, fmt: int, codes=None, gscale=None, rscale=None) -> W8A8We
                                      None if rscale is None else rscale.data_ptr(), N, K, fmt,
                                      _stream(W)), "rad_quant_weight_i8")
     return W8A8Weight(codes, gscale, rscale, fmt)
+
+
+def _bits16(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous GPU tensor" % name)
+    if t.dtype not in (torch.int16, torch.uint16, torch.bfloat16, torch.float16):
+        raise TypeError("%s must hold 16-bit values" % name)
+    return t
+
+
+def kv_quant_i8(x, codes=None, scale=None):
+    """int8 KV-cache encode of bf16 rows ``x`` [rows][D]: returns (codes, f16 scales)."""
+    torch = _torch()
+    _bits16(x, "x")
+    rows, D = x.shape
+    if codes is None:
+        codes = torch.empty((rows, D), dtype=torch.int8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float16, device=x.device)
+    _dev(codes, torch.int8, "codes")
+    _bits16(scale, "scale")
+    _check(lib().rad_kv_quant_i8(x.data_ptr(), codes.data_ptr(), scale.data_ptr(), rows, D, _stream(x)),
+           "rad_kv_quant_i8")
+    return codes, scale
+
+
+def kv_dequant_i8(codes, scale, y=None):
+    """Read an int8 KV cache back to bf16 [rows][D]."""
+    torch = _torch()
+    _dev(codes, torch.int8, "codes")
+    _bits16(scale, "scale")
+    rows, D = codes.shape
+    if y is None:
+        y = torch.empty((rows, D), dtype=torch.bfloat16, device=codes.device)
+    _bits16(y, "y")
+    _check(lib().rad_kv_dequant_i8(codes.data_ptr(), scale.data_ptr(), y.data_ptr(), rows, D,
+                                   _stream(codes)), "rad_kv_dequant_i8")
+    return y

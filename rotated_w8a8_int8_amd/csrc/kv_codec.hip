@@ -1,0 +1,191 @@
+// kv_codec.hip -- int8 KV-cache codec: bf16 head vectors <-> int8 codes with
+// one f16 scale per (token, head) (gfx950).
+//
+// What is computed (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance
+// container", section "Serve": kv-cache-dtype i8 keeps the attention cache as
+// int8 with an f16 scale per token and head):
+//   encode  s = f16_rne(amax / 127) over a row's D values (f32 division;
+//           subnormal f16 kept; saturated at 65504), codes =
+//           clamp(rne(x / s), -127, 127) with s the stored f16 value (f32
+//           division), s = 0 -> zero codes;
+//   decode  y = bf16_rne(code * s), the product exact in f32.
+//
+// Both kernels are HBM streams (3 bytes per element).  A row of D values is
+// held by D / 8 consecutive lanes, 8 values each (16 bytes of bf16, 8 bytes of
+// codes), so every load and store of a wave is one contiguous run.  Waves walk
+// the rows grid-stride, kUnroll row groups at a time with all loads issued
+// before any use.  The row amax is a DPP (and for D = 256 a cross-row
+// permute) max inside the row's lanes.  Codes go through x * fl(1/s), which
+// provably rounds like the IEEE quotient unless the product lies within 2^-13
+// of a half-integer; a wave with any such lane redoes its codes with the
+// division (|x / s| <= 127.06 here, so the product and the quotient differ
+// by less than 2^-15).
+#include "rad_device.h"
+#include "rad_launch.h"
+
+namespace rad {
+namespace {
+
+constexpr int kKvUnroll = 4;
+constexpr int kKvBlocks = 1024;
+
+struct Bf8 {
+    uint4 v;   // 8 bf16
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// f32 -> f16 bits, nearest even, subnormals kept, saturating at 65504.
+__device__ __forceinline__ uint32_t f16_sat_bits(float s) {
+    if (!(s < 65520.0f)) return 0x7BFFu;
+    const _Float16 h = static_cast<_Float16>(s);
+    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h));
+}
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+template <int L>
+__device__ __forceinline__ float row_max(float a) {
+    a = fmaxf(a, lane_xor<1>(a));
+    a = fmaxf(a, lane_xor<2>(a));
+    a = fmaxf(a, lane_xor<4>(a));
+    if constexpr (L >= 16) a = fmaxf(a, lane_xor<8>(a));
+    if constexpr (L >= 32) a = fmaxf(a, __shfl_xor(a, 16));
+    return a;
+}
+
+__device__ __forceinline__ float code_div(float x, float s) {
+    if (s == 0.0f) return 0.0f;
+    return fminf(fmaxf(__builtin_rintf(x / s), -127.0f), 127.0f);
+}
+__device__ __forceinline__ float code_rcp(float x, float rs, bool &near) {
+    const float t = x * rs;
+    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
+    return fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+}
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+    return (static_cast<uint32_t>(static_cast<int>(a)) & 0xFFu) |
+           ((static_cast<uint32_t>(static_cast<int>(b)) & 0xFFu) << 8) |
+           ((static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << 16) |
+           ((static_cast<uint32_t>(static_cast<int>(d)) & 0xFFu) << 24);
+}
+
+// D = 8 L values per row, 64 / L rows per wave per row group.
+template <int L>
+__global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restrict__ x,
+                                                       int8_t *__restrict__ codes,
+                                                       uint16_t *__restrict__ scale, int64_t rows) {
+    constexpr int D = 8 * L, RPW = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+    const int64_t ngroups = (rows + RPW - 1) / RPW;
+    const int rl = lane / L, cl = lane % L;
+    for (int64_t g0 = wave; g0 < ngroups; g0 += nwaves * kKvUnroll) {
+        uint4 v[kKvUnroll];
+#pragma unroll
+        for (int u = 0; u < kKvUnroll; ++u) {
+            const int64_t row = (g0 + u * nwaves) * RPW + rl;
+            v[u] = row < rows ? *reinterpret_cast<const uint4 *>(x + row * D + 8 * cl) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kKvUnroll; ++u) {
+            const int64_t row = (g0 + u * nwaves) * RPW + rl;
+            float f[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                          bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+            a = row_max<L>(a);
+            const uint32_t sb = f16_sat_bits(a / 127.0f);
+            const float s = f16_value(sb);
+            float q[8];
+            bool near = !(s >= 0x1p-120f);          // s = 0 (f16 scales are never above 65504)
+            const float rs = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = code_rcp(f[i], rs, near);
+            if (__any(near)) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = code_div(f[i], s);
+            }
+            if (row < rows) {
+                *reinterpret_cast<uint2 *>(codes + row * D + 8 * cl) =
+                    make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+                if (cl == 0) scale[row] = static_cast<uint16_t>(sb);
+            }
+        }
+    }
+}
+
+template <int L>
+__global__ __launch_bounds__(256) void kv_dequant_kernel(const int8_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ scale,
+                                                         uint16_t *__restrict__ y, int64_t rows) {
+    constexpr int D = 8 * L, RPW = 64 / L;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+    const int64_t ngroups = (rows + RPW - 1) / RPW;
+    const int rl = lane / L, cl = lane % L;
+    for (int64_t g0 = wave; g0 < ngroups; g0 += nwaves * kKvUnroll) {
+        uint2 c[kKvUnroll];
+        uint32_t sb[kKvUnroll];
+#pragma unroll
+        for (int u = 0; u < kKvUnroll; ++u) {
+            const int64_t row = (g0 + u * nwaves) * RPW + rl;
+            c[u] = row < rows ? *reinterpret_cast<const uint2 *>(codes + row * D + 8 * cl) : make_uint2(0, 0);
+            sb[u] = row < rows ? scale[row] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kKvUnroll; ++u) {
+            const int64_t row = (g0 + u * nwaves) * RPW + rl;
+            const float s = f16_value(sb[u]);
+            uint32_t o[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t w = h ? c[u].y : c[u].x;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float lo = static_cast<float>(static_cast<int8_t>((w >> (16 * j)) & 0xFFu)) * s;
+                    const float hi = static_cast<float>(static_cast<int8_t>((w >> (16 * j + 8)) & 0xFFu)) * s;
+                    o[2 * h + j] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+                }
+            }
+            if (row < rows) *reinterpret_cast<uint4 *>(y + row * D + 8 * cl) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    }
+}
+
+int kv_grid(int64_t rows, int D) {
+    const int64_t groups = (rows * D / 512 + 3) / 4;          // 4 waves per block, 64 lanes x 8 values
+    return static_cast<int>(groups < kKvBlocks ? (groups > 0 ? groups : 1) : kKvBlocks);
+}
+
+}  // namespace
+
+hipError_t launch_kv_quant(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D,
+                           hipStream_t st) {
+    const dim3 grid(kv_grid(rows, static_cast<int>(D))), block(256);
+    if (D == 64) hipLaunchKernelGGL(kv_quant_kernel<8>, grid, block, 0, st, x, codes, scale, rows);
+    else if (D == 128) hipLaunchKernelGGL(kv_quant_kernel<16>, grid, block, 0, st, x, codes, scale, rows);
+    else hipLaunchKernelGGL(kv_quant_kernel<32>, grid, block, 0, st, x, codes, scale, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_dequant(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows,
+                             int64_t D, hipStream_t st) {
+    const dim3 grid(kv_grid(rows, static_cast<int>(D))), block(256);
+    if (D == 64) hipLaunchKernelGGL(kv_dequant_kernel<8>, grid, block, 0, st, codes, scale, y, rows);
+    else if (D == 128) hipLaunchKernelGGL(kv_dequant_kernel<16>, grid, block, 0, st, codes, scale, y, rows);
+    else hipLaunchKernelGGL(kv_dequant_kernel<32>, grid, block, 0, st, codes, scale, y, rows);
+    return hipGetLastError();
+}
+
+}  // namespace rad

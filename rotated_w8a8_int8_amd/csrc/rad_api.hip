@@ -160,6 +160,33 @@ int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
                                                static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+int check_kv(const void *x, const void *codes, const void *scale, int64_t rows, int64_t D) {
+    if (rows < 0 || (D != 64 && D != 128 && D != 256)) return RAD_E_SHAPE;
+    if (rows > INT64_MAX / 2 / D) return RAD_E_RANGE;
+    if (rows == 0) return 1;
+    if (!x || !codes || !scale) return RAD_E_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scale, 2)) return RAD_E_ALIGN;
+    const Span xs = span(x, rows * D * 2), cs = span(codes, rows * D), ss = span(scale, rows * 2);
+    if (overlap(xs, cs) || overlap(xs, ss) || overlap(cs, ss)) return RAD_E_ALIAS;
+    return RAD_OK;
+}
+}  // namespace
+
+int rad_kv_quant_i8(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D,
+                    rad_stream_t stream) {
+    const int rc = check_kv(x, codes, scale, rows, D);
+    if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
+    return hip_status(rad::launch_kv_quant(x, codes, scale, rows, D, static_cast<hipStream_t>(stream)));
+}
+
+int rad_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows, int64_t D,
+                      rad_stream_t stream) {
+    const int rc = check_kv(y, codes, scale, rows, D);
+    if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
+    return hip_status(rad::launch_kv_dequant(codes, scale, y, rows, D, static_cast<hipStream_t>(stream)));
+}
+
 const char *rad_strerror(int status) {
     switch (status) {
         case RAD_OK: return "success";

@@ -29,6 +29,11 @@ hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const Weight
 constexpr int kQuantWeightMaxK = 32768;
 hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
                                int64_t N, int64_t K, int fmt, hipStream_t st);
+// int8 KV-cache codec; D is 64, 128 or 256.
+hipError_t launch_kv_quant(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D,
+                           hipStream_t st);
+hipError_t launch_kv_dequant(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows,
+                             int64_t D, hipStream_t st);
 hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st);
 

@@ -176,3 +176,28 @@ def test_quant_weight_validation():
     assert f(A, A + 4096, C, D, 4, 512, U8, None) == B.RAD_E_ALIAS   # codes inside W
     assert f(A, Bp, Bp + 512, D, 4, 512, U8, None) == B.RAD_E_ALIAS  # scales inside codes
     assert f(A, Bp, C, C + 4, 4, 512, U8, None) == B.RAD_E_ALIAS     # row scales over group scales
+
+
+# ------------------------------------------------------------- KV codec --
+
+@pytest.mark.parametrize("name", ["rad_kv_quant_i8", "rad_kv_dequant_i8"])
+def test_kv_validation(name):
+    f = getattr(B.lib(), name)
+    enc = name == "rad_kv_quant_i8"
+
+    def call(x=A, c=Bp, s=C, rows=10, D=128):
+        return f(x, c, s, rows, D, None) if enc else f(c, s, x, rows, D, None)
+
+    for D in (0, 32, 96, 100, 512):
+        assert call(D=D) == B.RAD_E_SHAPE
+    assert call(rows=-1) == B.RAD_E_SHAPE
+    assert call(rows=1 << 62) == B.RAD_E_RANGE
+    assert call(x=None, c=None, s=None, rows=0) == B.RAD_OK
+    assert call(x=None) == B.RAD_E_NULL
+    assert call(c=None) == B.RAD_E_NULL
+    assert call(s=None) == B.RAD_E_NULL
+    assert call(x=A + 8) == B.RAD_E_ALIGN
+    assert call(c=Bp + 4) == B.RAD_E_ALIGN
+    assert call(s=C + 1) == B.RAD_E_ALIGN
+    assert call(c=A + 1024) == B.RAD_E_ALIAS
+    assert call(s=Bp + 64) == B.RAD_E_ALIAS

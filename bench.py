@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
     python bench.py --op quant_weight [--workload NAME]
+    python bench.py --op kv_quant | kv_dequant [--workload kv_200k]
 
 A step is one pass of the whole layer over one batch of synthetic input that
 is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
@@ -30,6 +31,12 @@ scales out); the kernel is bound by its scale search on the vector ALUs, so
 (multiply by the reciprocal, round, two clamps, scale times code, subtract,
 square, accumulate) against the vector ALU peak without packed FP32 math:
 256 CUs x 64 lanes x 2.4 GHz = 39.3 T lane-operations per second.
+
+--op kv_quant / kv_dequant time the int8 KV-cache codec on a cache of
+synthetic bf16 head vectors (default kv_200k: 200K tokens x 8 heads x 128):
+encode reads bf16 and writes codes and f16 scales, decode the reverse; both
+are HBM streams, so `roofline` is their algorithmic bytes per second against
+the 8 TB/s HBM peak.
 """
 from __future__ import annotations
 
@@ -58,9 +65,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_gate_up")
-    ap.add_argument("--op", choices=("linear", "quant_weight"), default="linear",
+    ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant"),
+                    default="linear",
                     help="linear: the whole layer (default); quant_weight: the weight-side "
-                         "quantiser on the workload's weight shape")
+                         "quantiser on the workload's weight shape; kv_quant / kv_dequant: "
+                         "the int8 KV-cache codec (workload kv_200k or kv_tiny)")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -214,6 +223,9 @@ def main():
         return
     B.lib()                                            # fail loudly if not built
 
+    if args.op in ("kv_quant", "kv_dequant"):
+        bench_kv(args)
+        return
     wl = W.WORKLOADS[args.workload]
     if args.op == "quant_weight":
         bench_quant_weight(args, wl)
@@ -461,6 +473,107 @@ def bench_quant_weight(args, wl):
         "data": "synthetic",
         "config": {"workload": "quant_weight_" + wl.name, "N": N, "K": K,
                    "format": "u8g256_bf16row" if fmt == W.FMT_U8G256_BF16ROW else "bf16g128",
+                   "launch": "eager", "host_ms_per_step": round((t1 - t0) * 1e3 / steps, 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_on_timed_buffers": parity,
+    }))
+
+
+def bench_kv(args):
+    """rad_kv_quant_i8 or rad_kv_dequant_i8 on a cache of synthetic bf16 rows."""
+    import torch
+    import oracle
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
+    name = args.workload if args.workload in W.KV_WORKLOADS else "kv_200k"
+    rows, D = W.KV_WORKLOADS[name]
+    enc = args.op == "kv_quant"
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 20
+    x = W.make_kv(rows, D, seed=0)
+    dev = torch.device("cuda", 0)
+    # enough distinct copies that the 256 MiB last-level cache cannot serve repeats
+    per = rows * D * 3 + rows * 2
+    ncopies = max(1, min(8, -(-COPY_TARGET_BYTES // per)))
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev) for _ in range(ncopies)]
+    cs = [torch.empty((rows, D), dtype=torch.int8, device=dev) for _ in range(ncopies)]
+    ss = [torch.empty((rows,), dtype=torch.float16, device=dev) for _ in range(ncopies)]
+    ys = [torch.empty((rows, D), dtype=torch.bfloat16, device=dev) for _ in range(ncopies)]
+    for i in range(ncopies):
+        B.kv_quant_i8(xs[i], cs[i], ss[i])
+
+    def call(i):
+        if enc:
+            B.kv_quant_i8(xs[i], cs[i], ss[i])
+        else:
+            B.kv_dequant_i8(cs[i], ss[i], ys[i])
+
+    stream = torch.cuda.Stream(device=dev)             # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i % ncopies)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(steps):
+            call(i % ncopies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / steps
+    alg = rows * D * 2 + rows * D + rows * 2
+    value = alg / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "rad_kv_quant_i8" if enc else "rad_kv_dequant_i8",
+            "bytes_per_launch": alg, "us_per_launch": round(ms * 1e3, 3)}
+    torch.cuda.synchronize()
+    sample = np.unique(np.linspace(0, rows - 1, 4096).astype(int))
+    co, so = oracle.kv_quant_i8(x[sample])
+    parity = True
+    for i in range(ncopies):
+        parity = parity and bool(np.array_equal(cs[i].cpu().numpy()[sample], co))
+        parity = parity and bool(np.array_equal(ss[i].cpu().view(torch.int16).numpy().view(np.uint16)[sample], so))
+        if not enc:
+            yo = oracle.kv_dequant_i8(co, so)
+            parity = parity and bool(np.array_equal(ys[i].cpu().view(torch.int16).numpy().view(np.uint16)[sample], yo))
+    cpu = None
+    if not args.no_cpu_baseline:
+        nrow = min(rows, 1 << 18)
+        xs_h = np.ascontiguousarray(x[:nrow])
+        co_h, so_h = oracle.kv_quant_i8(xs_h)
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            if enc:
+                oracle.kv_quant_i8(xs_h)
+            else:
+                oracle.kv_dequant_i8(co_h, so_h)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - c0) / n
+        cpu = {"value": round(alg * nrow / rows / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": "%d of %d rows, %d repetitions, %.1f s" % (nrow, rows, n, dt * n)}
+    print(json.dumps({
+        "metric": "int8 KV-cache codec: HBM GB/s (bf16 rows <-> int8 codes + f16 scale per token and head)",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s_%s" % (args.op, name), "rows": rows, "D": D, "copies": ncopies,
                    "launch": "eager", "host_ms_per_step": round((t1 - t0) * 1e3 / steps, 5)},
         "roofline": roof,
         "cpu_baseline": cpu,

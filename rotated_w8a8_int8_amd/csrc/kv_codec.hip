@@ -13,8 +13,9 @@
 // Both kernels are HBM streams (3 bytes per element).  A row of D values is
 // held by D / 8 consecutive lanes, 8 values each (16 bytes of bf16, 8 bytes of
 // codes), so every load and store of a wave is one contiguous run.  Waves walk
-// the rows grid-stride, kUnroll row groups at a time with all loads issued
-// before any use.  The row amax is a DPP (and for D = 256 a cross-row
+// the rows grid-stride, kKvUnroll row groups at a time with all loads issued
+// before any use (2 groups and 4096 workgroups measured best on MI355X among
+// 2/4/8 x 1024/2048/4096).  The row amax is a DPP (and for D = 256 a cross-row
 // permute) max inside the row's lanes.  Codes go through x * fl(1/s), which
 // provably rounds like the IEEE quotient unless the product lies within 2^-13
 // of a half-integer; a wave with any such lane redoes its codes with the
@@ -26,12 +27,8 @@
 namespace rad {
 namespace {
 
-constexpr int kKvUnroll = 4;
-constexpr int kKvBlocks = 1024;
-
-struct Bf8 {
-    uint4 v;   // 8 bf16
-};
+constexpr int kKvUnroll = 2;
+constexpr int kKvBlocks = 4096;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

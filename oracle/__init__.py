@@ -72,9 +72,10 @@ def _load():
         lib.orc_quant_weight_i8.argtypes = [p, p, p, p, i64, i64, ci]
         lib.orc_kv_quant_i8.argtypes = [p, p, p, i64, i64]
         lib.orc_kv_dequant_i8.argtypes = [p, p, p, i64, i64]
+        lib.orc_rescore.argtypes = [p, p, p, ci, p, p, p, p, i64, i64, i64, i64]
         for f in (lib.orc_fwht128, lib.orc_quant_act_i8, lib.orc_group_partials,
                   lib.orc_epilogue, lib.orc_linear, lib.orc_quant_weight_i8,
-                  lib.orc_kv_quant_i8, lib.orc_kv_dequant_i8):
+                  lib.orc_kv_quant_i8, lib.orc_kv_dequant_i8, lib.orc_rescore):
             f.restype = ci
         _lib = lib
     return _lib
@@ -213,4 +214,24 @@ def kv_dequant_i8(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     rows, D = codes.shape
     y = np.empty((rows, D), np.uint16)
     _check(_load().orc_kv_dequant_i8(_ptr(codes), _ptr(scale), _ptr(y), rows, D))
+    return y
+
+
+def rescore(qx: np.ndarray, s: np.ndarray, qw: np.ndarray, fmt: int, gscale: np.ndarray,
+            rscale: np.ndarray | None, ids: np.ndarray) -> np.ndarray:
+    """Outputs of the layer at candidate rows only: y[m][j] = linear(...)[m][ids[m][j]]
+    (NaN for an id outside 0..N-1).  ids: int32 [M][C]."""
+    qx = _c(qx, np.int8)
+    s = _c(s, np.float32)
+    qw = _c(qw, np.int8)
+    gscale = _c(gscale, np.uint8 if fmt == FMT_U8G256_BF16ROW else np.uint16)
+    if rscale is not None:
+        rscale = _c(rscale, np.uint16)
+    ids = _c(ids, np.int32)
+    M, K = qx.shape
+    N = qw.shape[0]
+    C = ids.shape[1]
+    y = np.empty((M, C), np.float32)
+    _check(_load().orc_rescore(_ptr(qx), _ptr(s), _ptr(qw), fmt, _ptr(gscale), _ptr(rscale), _ptr(ids),
+                               _ptr(y), M, C, N, K))
     return y

@@ -524,3 +524,49 @@ int orc_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, i
     }
     return ORC_OK;
 }
+
+/*
+ * ---- Rescoring drafted candidates against the int8 head ----
+ *
+ * Source: model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance container",
+ * table row "Speculator": the drafter's vocabulary head proposes its top 32
+ * candidates and the engine rescores them against the model's own head (the
+ * int8 head of table row "Weights").
+ *   R14 Rescoring computes, for each token m and each candidate row
+ *       ids[m][j], exactly the output the full layer would give at that row
+ *       (same partials, same epilogue), y[m][j] = linear(q, s, W)[m][ids[m][j]].
+ *       A candidate id outside 0..N-1 yields NaN.
+ */
+int orc_rescore(const int8_t *qx, const float *s, const int8_t *qw, int fmt, const void *gscale,
+                const uint16_t *rscale, const int32_t *ids, float *y, int64_t M, int64_t C,
+                int64_t N, int64_t K)
+{
+    int64_t gw = group_width(fmt);
+    if (!qx || !s || !qw || !gscale || !ids || !y || gw == 0 || M < 0 || C < 0 || N < 0 ||
+        K <= 0 || K % gw != 0)
+        return ORC_E_ARG;
+    if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
+    int64_t G = K / gw;
+    if (G > 4096) return ORC_E_ARG;
+    size_t esz = (fmt == ORC_FMT_U8G256_BF16ROW) ? 1 : 2;
+    int status = ORC_OK;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t j = 0; j < C; ++j) {
+            int64_t n = ids[m * C + j];
+            if (n < 0 || n >= N) {
+                y[m * C + j] = NAN;
+                continue;
+            }
+            int32_t Prow[4096];
+            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, Prow);
+            if (rc != ORC_OK) {
+                #pragma omp critical
+                status = rc;
+                continue;
+            }
+            y[m * C + j] = pair_output(fmt, Prow, G, s[m], (const char *)gscale + (size_t)(n * G) * esz,
+                                       fmt == ORC_FMT_U8G256_BF16ROW ? rscale + n : NULL);
+        }
+    return status;
+}

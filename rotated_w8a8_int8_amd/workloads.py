@@ -161,3 +161,11 @@ def make_kv(rows: int, D: int, seed: int = 0, outlier_frac: float = 0.01,
     v[mask] *= np.float32(outlier_mul)
     v *= np.exp(rng.uniform(-4.0, 4.0, size=rows)).astype(np.float32)[:, None]
     return f32_to_bf16_bits(v)
+
+
+def make_candidates(M: int, N: int, C: int = 32, seed: int = 0) -> np.ndarray:
+    """Candidate row ids int32 [M][C], distinct within a token, drawn with one
+    ``numpy.random.Generator(PCG64(seed))``: for each token in order,
+    ``choice(N, C, replace=False)``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.stack([rng.choice(N, size=C, replace=False) for _ in range(M)]).astype(np.int32)

@@ -222,6 +222,26 @@ int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
                         int64_t K, int32_t fmt, rad_stream_t stream);
 
 /*
+ * rad_w8a8_rescore -- the layer's output at candidate rows only (model card
+ * "Qwen3.8-27B IQ8R + DFlash2 -- radiance container", table row "Speculator":
+ * the drafter's top 32 candidates are rescored against the model's own int8
+ * head, table row "Weights").
+ *
+ *   q, scale  activation codes [M][K] and scales [M] as for rad_w8a8_gemv.
+ *   w         the weight descriptor (either format).
+ *   ids       int32 [M][C] candidate rows per token, 4-byte aligned.
+ *   y         f32 [M][C] output, 4-byte aligned.
+ *   M, C >= 0, M * C < 2^33.
+ *
+ * y[m][j] equals the output rad_w8a8_gemv / rad_w8a8_gemm would give at row
+ * ids[m][j] (same exact partials and epilogue; for the u8 format the very same
+ * bits as the one-token path, rounded once from f64).  An id outside 0..N-1
+ * reads nothing and gives NaN.  y may not overlap any input (RAD_E_ALIAS).
+ */
+int rad_w8a8_rescore(const int8_t *q, const float *scale, const rad_w8a8_weight *w, const int32_t *ids,
+                     int64_t C, float *y, int64_t M, rad_stream_t stream);
+
+/*
  * rad_kv_quant_i8 / rad_kv_dequant_i8 -- the int8 attention-cache codec
  * (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance container", section
  * "Serve": kv-cache-dtype i8 stores the attention cache as int8 with an f16

@@ -33,7 +33,8 @@ RAD_GEMV_MAX_M = 128
 RAD_QUANT_WEIGHT_MAX_K = 32768
 
 EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
-           "rad_quant_weight_i8", "rad_kv_quant_i8", "rad_kv_dequant_i8", "rad_strerror")
+           "rad_quant_weight_i8", "rad_kv_quant_i8", "rad_kv_dequant_i8", "rad_w8a8_rescore",
+           "rad_strerror")
 KV_HEAD_DIMS = (64, 128, 256)
 
 
@@ -74,8 +75,10 @@ def lib() -> ctypes.CDLL:
         L.rad_quant_weight_i8.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_int32, vp]
         L.rad_kv_quant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
         L.rad_kv_dequant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.rad_w8a8_rescore.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, i64, vp]
         for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm,
-                  L.rad_w8a8_linear, L.rad_quant_weight_i8, L.rad_kv_quant_i8, L.rad_kv_dequant_i8):
+                  L.rad_w8a8_linear, L.rad_quant_weight_i8, L.rad_kv_quant_i8, L.rad_kv_dequant_i8,
+                  L.rad_w8a8_rescore):
             f.restype = ci
         L.rad_strerror.argtypes = [ci]
         L.rad_strerror.restype = ctypes.c_char_p
@@ -293,4 +296,22 @@ def kv_dequant_i8(codes, scale, y=None):
     _bits16(y, "y")
     _check(lib().rad_kv_dequant_i8(codes.data_ptr(), scale.data_ptr(), y.data_ptr(), rows, D,
                                    _stream(codes)), "rad_kv_dequant_i8")
+    return y
+
+
+def w8a8_rescore(q, scale, w: W8A8Weight, ids, y=None):
+    """The layer's outputs at candidate rows ``ids`` (int32 [M][C]) only: y [M][C]."""
+    torch = _torch()
+    _dev(q, torch.int8, "q")
+    _dev(scale, torch.float32, "scale")
+    _dev(ids, torch.int32, "ids")
+    M, C = ids.shape
+    if q.shape[0] != M or q.shape[1] != w.K:
+        raise ValueError("q is %s, expected [%d, %d]" % (tuple(q.shape), M, w.K))
+    if y is None:
+        y = torch.empty((M, C), dtype=torch.float32, device=q.device)
+    _dev(y, torch.float32, "y")
+    d = w.desc()
+    _check(lib().rad_w8a8_rescore(q.data_ptr(), scale.data_ptr(), ctypes.byref(d), ids.data_ptr(), C,
+                                  y.data_ptr(), M, _stream(q)), "rad_w8a8_rescore")
     return y

@@ -160,6 +160,33 @@ int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
                                                static_cast<hipStream_t>(stream)));
 }
 
+int rad_w8a8_rescore(const int8_t *q, const float *scale, const rad_w8a8_weight *w, const int32_t *ids,
+                     int64_t C, float *y, int64_t M, rad_stream_t stream) {
+    if (!w) return RAD_E_NULL;
+    const int gw = group_width(w->fmt);
+    if (gw == 0) return RAD_E_FMT;
+    if (w->fmt == RAD_FMT_U8G256_BF16ROW && !w->rscale) return RAD_E_FMT;
+    if (w->fmt == RAD_FMT_BF16G128 && w->rscale) return RAD_E_FMT;
+    if (M < 0 || C < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
+    if (w->N > kI32Max || w->K > kI32Max || C > kI32Max || M > kI32Max || M * C >= (int64_t(1) << 33))
+        return RAD_E_RANGE;
+    if (M == 0 || C == 0) return RAD_OK;
+    if (!q || !scale || !ids || !y || !w->codes || !w->gscale) return RAD_E_NULL;
+    if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(w->gscale, 4) ||
+        (w->rscale && !aligned(w->rscale, 4)) || !aligned(scale, 4) || !aligned(ids, 4) || !aligned(y, 4))
+        return RAD_E_ALIGN;
+    const int64_t N = w->N, K = w->K, G = K / gw;
+    const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
+    const Span in[] = {span(q, M * K), span(scale, M * 4), span(w->codes, N * K),
+                       span(w->gscale, N * G * esz), w->rscale ? span(w->rscale, N * 2) : Span{0, 0},
+                       span(ids, M * C * 4)};
+    const Span ys = span(y, M * C * 4);
+    for (const Span &sp : in)
+        if (overlap(ys, sp)) return RAD_E_ALIAS;
+    return hip_status(rad::launch_rescore(q, scale, weight_args(w), ids, C, y, M,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 int check_kv(const void *x, const void *codes, const void *scale, int64_t rows, int64_t D) {
     if (rows < 0 || (D != 64 && D != 128 && D != 256)) return RAD_E_SHAPE;

@@ -29,6 +29,9 @@ hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const Weight
 constexpr int kQuantWeightMaxK = 32768;
 hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
                                int64_t N, int64_t K, int fmt, hipStream_t st);
+// The layer at candidate rows ids [M][C] only.
+hipError_t launch_rescore(const int8_t *q, const float *s, const WeightArgs &w, const int32_t *ids,
+                          int64_t C, float *y, int64_t M, hipStream_t st);
 // int8 KV-cache codec; D is 64, 128 or 256.
 hipError_t launch_kv_quant(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t rows, int64_t D,
                            hipStream_t st);

@@ -201,3 +201,25 @@ def test_kv_validation(name):
     assert call(s=C + 1) == B.RAD_E_ALIGN
     assert call(c=A + 1024) == B.RAD_E_ALIAS
     assert call(s=Bp + 64) == B.RAD_E_ALIAS
+
+
+# ------------------------------------------------------------ rescoring --
+
+def test_rescore_validation():
+    f = B.lib().rad_w8a8_rescore
+    E2 = 0x7F6000000000
+
+    def call(d, M=4, C=32, q=A, s=Bp, ids=E2, y=F):
+        return f(q, s, None if d is None else ctypes.byref(d), ids, C, y, M, None)
+
+    assert call(None) == B.RAD_E_NULL
+    assert call(desc(fmt=5)) == B.RAD_E_FMT
+    assert call(desc(K=384)) == B.RAD_E_SHAPE
+    assert call(desc(), C=-1) == B.RAD_E_SHAPE
+    assert call(desc(), M=1 << 20, C=1 << 14) == B.RAD_E_RANGE
+    assert call(desc(), M=0, q=0, s=0, ids=0, y=0) == B.RAD_OK
+    assert call(desc(), C=0, ids=0, y=0) == B.RAD_OK
+    assert call(desc(), ids=0) == B.RAD_E_NULL
+    assert call(desc(), ids=E2 + 2) == B.RAD_E_ALIGN
+    assert call(desc(), y=E2 + 64) == B.RAD_E_ALIAS                 # y over ids
+    assert call(desc(), y=C + 128) == B.RAD_E_ALIAS                 # y over codes

@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--eager]
     python bench.py --op quant_weight [--workload NAME]
     python bench.py --op kv_quant | kv_dequant [--workload kv_200k]
+    python bench.py --op rescore [--workload vocab_head]
 
 A step is one pass of the whole layer over one batch of synthetic input that
 is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
@@ -37,6 +38,12 @@ synthetic bf16 head vectors (default kv_200k: 200K tokens x 8 heads x 128):
 encode reads bf16 and writes codes and f16 scales, decode the reverse; both
 are HBM streams, so `roofline` is their algorithmic bytes per second against
 the 8 TB/s HBM peak.
+
+--op rescore times rad_w8a8_rescore on the workload's weight (default the
+vocabulary head) with 32 distinct candidate rows per token: 64 different
+candidate sets are cycled through a HIP graph so the gathered rows come from
+HBM, and the bytes are the gathered rows with their scales plus the codes,
+scales, ids and outputs.
 """
 from __future__ import annotations
 
@@ -65,11 +72,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_gate_up")
-    ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant"),
+    ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore"),
                     default="linear",
                     help="linear: the whole layer (default); quant_weight: the weight-side "
                          "quantiser on the workload's weight shape; kv_quant / kv_dequant: "
-                         "the int8 KV-cache codec (workload kv_200k or kv_tiny)")
+                         "the int8 KV-cache codec (workload kv_200k or kv_tiny); rescore: "
+                         "32 candidate rows per token of the workload's weight")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -229,6 +237,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.op == "quant_weight":
         bench_quant_weight(args, wl)
+        return
+    if args.op == "rescore":
+        bench_rescore(args, W.WORKLOADS["vocab_head"] if args.workload == "decode_gate_up" else wl)
         return
     sz = sizes(wl)
     big = wl.M > B.RAD_GEMV_MAX_M
@@ -474,6 +485,103 @@ def bench_quant_weight(args, wl):
         "config": {"workload": "quant_weight_" + wl.name, "N": N, "K": K,
                    "format": "u8g256_bf16row" if fmt == W.FMT_U8G256_BF16ROW else "bf16g128",
                    "launch": "eager", "host_ms_per_step": round((t1 - t0) * 1e3 / steps, 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_on_timed_buffers": parity,
+    }))
+
+
+def bench_rescore(args, wl):
+    """rad_w8a8_rescore: the layer at 32 candidate rows per token."""
+    import torch
+    import oracle
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
+    C, nsets = 32, 64
+    steps = args.steps if args.steps is not None else 6400
+    warmup = args.warmup if args.warmup is not None else 640
+    inp = W.make_workload(wl.name, seed=0)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    w = B.W8A8Weight(to_dev(inp.qw), to_dev(inp.gscale), None if inp.rscale is None else to_dev(inp.rscale),
+                     inp.fmt)
+    q, s = B.quant_act_i8(to_dev(inp.x))
+    ids_h = [W.make_candidates(wl.M, wl.N, C, seed=i) for i in range(nsets)]
+    ids = [to_dev(a) for a in ids_h]
+    ys = [torch.empty((wl.M, C), dtype=torch.float32, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.Stream(device=dev)             # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(nsets):
+            B.w8a8_rescore(q, s, w, ids[i], y=ys[i])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(nsets):
+            B.w8a8_rescore(q, s, w, ids[i], y=ys[i])
+    torch.cuda.synchronize()
+    rounds = max(1, steps // nsets)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // nsets)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(rounds):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (rounds * nsets)
+    esz = 1 if wl.fmt == W.FMT_U8G256_BF16ROW else 2
+    row = wl.K + wl.G * esz + (2 if wl.fmt == W.FMT_U8G256_BF16ROW else 0)
+    alg = wl.M * C * row + wl.M * wl.K + wl.M * 4 + wl.M * C * 4 * 2
+    value = alg / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "rad_w8a8_rescore",
+            "bytes_per_launch": alg, "us_per_launch": round(ms * 1e3, 3)}
+    qh, sh = q.cpu().numpy(), s.cpu().numpy()
+    parity = True
+    for i in (0, nsets - 1):
+        yo = oracle.rescore(qh, sh, inp.qw, wl.fmt, inp.gscale, inp.rscale, ids_h[i])
+        yg = ys[i].cpu().numpy().astype(np.float64)
+        nrm = np.linalg.norm(yo.astype(np.float64), axis=1, keepdims=True)
+        parity = parity and bool(np.max(np.abs(yg - yo) / nrm) <= 1e-5)
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            oracle.rescore(qh, sh, inp.qw, wl.fmt, inp.gscale, inp.rscale, ids_h[n % nsets])
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - c0) / n
+        cpu = {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": "whole call (%d tokens x %d candidates), %d repetitions, %.1f s"
+                                           % (wl.M, C, n, dt * n)}
+    print(json.dumps({
+        "metric": "rescoring 32 drafted candidates per token against the int8 head: HBM GB/s",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": rounds * nsets,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "rescore_" + wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "candidates": C,
+                   "candidate_sets": nsets, "launch": "hip_graph"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_on_timed_buffers": parity,

@@ -25,7 +25,7 @@ namespace rad {
 namespace {
 
 constexpr int kFmtU8 = 0;
-constexpr int kRsPass = 4;     // chunks per lane per pass
+constexpr int kRsPass = 8;     // chunks per lane per pass (K = 8192 in one pass)
 
 __device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int x) {
     const int lo = static_cast<int>(v & 0xFFFFFFFF), hi = static_cast<int>(v >> 32);

@@ -30,7 +30,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FMT_U8G256_BF16ROW = 0
 FMT_BF16G128 = 1
-GROUP_WIDTH = {FMT_U8G256_BF16ROW: 256, FMT_BF16G128: 128}
+FMT_TBL4_BF16G128 = 2          # 4-bit indices into the drafter's codebook, packed
+GROUP_WIDTH = {FMT_U8G256_BF16ROW: 256, FMT_BF16G128: 128, FMT_TBL4_BF16G128: 128}
 
 _ERRORS = {
     -1: "invalid argument",
@@ -73,9 +74,10 @@ def _load():
         lib.orc_kv_quant_i8.argtypes = [p, p, p, i64, i64]
         lib.orc_kv_dequant_i8.argtypes = [p, p, p, i64, i64]
         lib.orc_rescore.argtypes = [p, p, p, ci, p, p, p, p, i64, i64, i64, i64]
+        lib.orc_tbl4_unpack.argtypes = [p, p, i64, i64]
         for f in (lib.orc_fwht128, lib.orc_quant_act_i8, lib.orc_group_partials,
                   lib.orc_epilogue, lib.orc_linear, lib.orc_quant_weight_i8,
-                  lib.orc_kv_quant_i8, lib.orc_kv_dequant_i8, lib.orc_rescore):
+                  lib.orc_kv_quant_i8, lib.orc_kv_dequant_i8, lib.orc_rescore, lib.orc_tbl4_unpack):
             f.restype = ci
         _lib = lib
     return _lib
@@ -120,14 +122,34 @@ def quant_act_i8(x: np.ndarray, rotate: bool = True):
     return q, s
 
 
+def _wcodes(qw, fmt, K):
+    """Weight codes: int8 [N][K], or packed 4-bit indices uint8 [N][K/2]."""
+    if fmt == FMT_TBL4_BF16G128:
+        qw = _c(qw, np.uint8)
+        if qw.shape[1] * 2 != K:
+            raise ValueError("packed codes must be [N][K/2]")
+    else:
+        qw = _c(qw, np.int8)
+        if qw.shape[1] != K:
+            raise ValueError("K mismatch")
+    return qw
+
+
+def tbl4_unpack(packed: np.ndarray, K: int) -> np.ndarray:
+    """Table values int8 [N][K] of packed 4-bit indices uint8 [N][K/2]."""
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    out = np.empty((N, K), np.int8)
+    _check(_load().orc_tbl4_unpack(_ptr(packed), _ptr(out), N, K))
+    return out
+
+
 def group_partials(qx: np.ndarray, qw: np.ndarray, fmt: int) -> np.ndarray:
     """int32 P[m][n][g]: exact sums of q_x*q_w over each K group."""
     qx = _c(qx, np.int8)
-    qw = _c(qw, np.int8)
     M, K = qx.shape
-    N, K2 = qw.shape
-    if K != K2:
-        raise ValueError("K mismatch")
+    qw = _wcodes(qw, fmt, K)
+    N = qw.shape[0]
     G = K // GROUP_WIDTH[fmt]
     P = np.empty((M, N, G), np.int32)
     _check(_load().orc_group_partials(_ptr(qx), _ptr(qw), _ptr(P), M, N, K, fmt))
@@ -153,11 +175,11 @@ def linear(qx: np.ndarray, s: np.ndarray, qw: np.ndarray, fmt: int, gscale: np.n
     """f32 y[m][n] straight from codes, without storing the partials."""
     qx = _c(qx, np.int8)
     s = _c(s, np.float32)
-    qw = _c(qw, np.int8)
     gscale = _c(gscale, np.uint8 if fmt == FMT_U8G256_BF16ROW else np.uint16)
     if rscale is not None:
         rscale = _c(rscale, np.uint16)
     M, K = qx.shape
+    qw = _wcodes(qw, fmt, K)
     N = qw.shape[0]
     y = np.empty((M, N), np.float32)
     _check(_load().orc_linear(_ptr(qx), _ptr(s), _ptr(qw), fmt, _ptr(gscale), _ptr(rscale),
@@ -178,14 +200,15 @@ WQ_CANDIDATES = 16
 
 
 def quant_weight_i8(W: np.ndarray, fmt: int):
-    """Rotate float weights ``W`` [N][K] per 128-block and quantise them to int8
-    with a searched scale per group.  Returns (codes int8 [N][K], gscale
-    (uint8 [N][K/256] or bf16 bits uint16 [N][K/128]), rscale (bf16 bits
-    uint16 [N] for the u8 format, else None))."""
+    """Rotate float weights ``W`` [N][K] per 128-block and quantise them with a
+    searched scale per group.  Returns (codes int8 [N][K], or packed 4-bit
+    table indices uint8 [N][K/2] for the table format; gscale (uint8
+    [N][K/256] or bf16 bits uint16 [N][K/128]); rscale (bf16 bits uint16 [N]
+    for the u8 format, else None))."""
     W = _c(W, np.float32)
     N, K = W.shape
     G = K // GROUP_WIDTH[fmt]
-    codes = np.empty((N, K), np.int8)
+    codes = np.empty((N, K // 2), np.uint8) if fmt == FMT_TBL4_BF16G128 else np.empty((N, K), np.int8)
     if fmt == FMT_U8G256_BF16ROW:
         gscale = np.empty((N, G), np.uint8)
         rscale = np.empty((N,), np.uint16)
@@ -223,12 +246,12 @@ def rescore(qx: np.ndarray, s: np.ndarray, qw: np.ndarray, fmt: int, gscale: np.
     (NaN for an id outside 0..N-1).  ids: int32 [M][C]."""
     qx = _c(qx, np.int8)
     s = _c(s, np.float32)
-    qw = _c(qw, np.int8)
     gscale = _c(gscale, np.uint8 if fmt == FMT_U8G256_BF16ROW else np.uint16)
     if rscale is not None:
         rscale = _c(rscale, np.uint16)
     ids = _c(ids, np.int32)
     M, K = qx.shape
+    qw = _wcodes(qw, fmt, K)
     N = qw.shape[0]
     C = ids.shape[1]
     y = np.empty((M, C), np.float32)

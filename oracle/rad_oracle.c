@@ -56,6 +56,33 @@
 
 #define ORC_FMT_U8G256_BF16ROW 0
 #define ORC_FMT_BF16G128       1
+#define ORC_FMT_TBL4_BF16G128  2
+
+/*
+ * The drafter's 16-level integer codebook, as printed in the recipe rules of
+ * section "How this file was made" (rules dflash.fc / dflash.blk.*: rtn
+ * table=... group=128 scale=bf16 transform=fwht128 rule=search), and its
+ * packing (reading R15, the card gives none): codes are 4-bit indices into
+ * this table, two per byte; in each 16-byte run of a packed row, byte b holds
+ * element 32c + b in its low nibble and element 32c + 16 + b in its high
+ * nibble (c the run's index).  The layer is then exactly the head format
+ * (bf16 scale per (row, 128 of K)) applied to the table values.
+ */
+static const int8_t TBL4[16] = {-127, -97, -75, -58, -43, -30, -18, -6,
+                                 6, 18, 30, 43, 58, 75, 97, 127};
+
+int orc_tbl4_unpack(const uint8_t *packed, int8_t *out, int64_t rows, int64_t K)
+{
+    if (!packed || !out || rows < 0 || K <= 0 || K % 32 != 0) return -1;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < K / 32; ++c)
+            for (int b = 0; b < 16; ++b) {
+                uint8_t v = packed[r * (K / 2) + 16 * c + b];
+                out[r * K + 32 * c + b] = TBL4[v & 15];
+                out[r * K + 32 * c + 16 + b] = TBL4[v >> 4];
+            }
+    return 0;
+}
 
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
@@ -168,8 +195,17 @@ static int pair_partials(const int8_t *qx, const int8_t *qw, int64_t K, int64_t 
 static int64_t group_width(int fmt)
 {
     if (fmt == ORC_FMT_U8G256_BF16ROW) return 256;
-    if (fmt == ORC_FMT_BF16G128) return 128;
+    if (fmt == ORC_FMT_BF16G128 || fmt == ORC_FMT_TBL4_BF16G128) return 128;
     return 0;
+}
+
+/* Weight row n as int8 values: the codes themselves, or the table values of
+ * the packed indices (unpacked into tmp, K bytes). */
+static const int8_t *weight_row(const int8_t *qw, int fmt, int64_t n, int64_t K, int8_t *tmp)
+{
+    if (fmt != ORC_FMT_TBL4_BF16G128) return qw + n * K;
+    orc_tbl4_unpack((const uint8_t *)qw + n * (K / 2), tmp, 1, K);
+    return tmp;
 }
 
 /* Epilogue of reading R6 for one output element. */
@@ -201,10 +237,12 @@ int orc_group_partials(const int8_t *qx, const int8_t *qw, int32_t *P,
     if (!qx || !qw || !P || gw == 0 || M < 0 || N < 0 || K <= 0 || K % gw != 0) return ORC_E_ARG;
     int64_t G = K / gw;
     int status = ORC_OK;
+    if (K > 65536) return ORC_E_ARG;
     #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
-            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, P + (m * N + n) * G);
+            int8_t tmp[65536];
+            int rc = pair_partials(qx + m * K, weight_row(qw, fmt, n, K, tmp), K, gw, P + (m * N + n) * G);
             if (rc != ORC_OK) {
                 #pragma omp critical
                 status = rc;
@@ -246,14 +284,15 @@ int orc_linear(const int8_t *qx, const float *s, const int8_t *qw, int fmt,
         return ORC_E_ARG;
     if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
     int64_t G = K / gw;
-    if (G > 4096) return ORC_E_ARG;
+    if (G > 4096 || K > 65536) return ORC_E_ARG;
     size_t esz = (fmt == ORC_FMT_U8G256_BF16ROW) ? 1 : 2;
     int status = ORC_OK;
     #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
             int32_t Prow[4096];
-            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, Prow);
+            int8_t tmp[65536];
+            int rc = pair_partials(qx + m * K, weight_row(qw, fmt, n, K, tmp), K, gw, Prow);
             if (rc != ORC_OK) {
                 #pragma omp critical
                 status = rc;
@@ -319,6 +358,30 @@ static float bf16_float(uint16_t bits)
     return c.f;
 }
 
+/*
+ * R16 The table format's "round to nearest": the index of the table entry
+ * nearest to t = w~ / d (f32 division), decided against the exact midpoints
+ * of neighbouring entries; a t exactly on a midpoint takes the entry of
+ * smaller magnitude, t = 0 (equally far from -6 and 6) takes 6; d = 0 gives
+ * the index of 6 (value 0 after scaling either way).
+ */
+static int tbl4_index(float w, float d)
+{
+    if (d == 0.0f) return 8;
+    float t = w / d;
+    int idx;
+    if (t >= 0.0f) {
+        idx = 8;
+        for (int i = 8; i < 15; ++i)
+            if (t > ((float)TBL4[i] + (float)TBL4[i + 1]) / 2.0f) idx = i + 1;
+    } else {
+        idx = 7;
+        for (int i = 7; i > 0; --i)
+            if (t < ((float)TBL4[i - 1] + (float)TBL4[i]) / 2.0f) idx = i - 1;
+    }
+    return idx;
+}
+
 static int8_t wq_code(float w, float d)
 {
     if (d == 0.0f) return 0;
@@ -340,9 +403,10 @@ static double wq_sq_err(const float *w, const int8_t *q, float d, int64_t n)
 
 /*
  * Quantise float weights W [N][K] (row-major, K % group == 0): rotate (R7),
- * then pick scales (R8-R10).  codes int8 [N][K]; gscale u8 [N][K/256] or bf16
- * bits [N][K/128]; rscale bf16 bits [N] for the u8 format (ignored, may be
- * NULL, for the head format).
+ * then pick scales (R8-R10).  codes int8 [N][K] (table format: packed 4-bit
+ * indices uint8 [N][K/2], R15-R16); gscale u8 [N][K/256] or bf16 bits
+ * [N][K/128]; rscale bf16 bits [N] for the u8 format (ignored, may be NULL,
+ * for the bf16-scaled formats).
  */
 int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
                         int64_t N, int64_t K, int fmt)
@@ -390,7 +454,7 @@ int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
         }
         for (int64_t g = 0; g < G; ++g) {
             const float *wg = wr + g * gw;
-            int8_t *out = codes + n * K + g * gw;
+            int8_t *out = (fmt == ORC_FMT_TBL4_BF16G128) ? NULL : codes + n * K + g * gw;
             float amax = 0.0f;
             for (int64_t k = 0; k < gw; ++k) {
                 float a = fabsf(wg[k]);
@@ -403,6 +467,18 @@ int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
                 float target = (amax * wq_alpha(c)) / 127.0f;
                 uint16_t stored;
                 float d;
+                if (fmt == ORC_FMT_TBL4_BF16G128) {
+                    stored = bf16_rne_bits(target);
+                    d = bf16_float(stored);
+                    for (int64_t k = 0; k < gw; ++k) qc[k] = TBL4[tbl4_index(wg[k], d)];
+                    double err = wq_sq_err(wg, qc, d, gw);
+                    if (best < 0 || err < best_err) {
+                        best = c;
+                        best_err = err;
+                        best_scale = stored;
+                    }
+                    continue;
+                }
                 if (fmt == ORC_FMT_U8G256_BF16ROW) {
                     float u = 1.0f;
                     if (r != 0.0f) {
@@ -426,7 +502,15 @@ int orc_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
             }
             /* the winner's codes, recomputed from its scale */
             float d = (fmt == ORC_FMT_U8G256_BF16ROW) ? r * (float)best_scale : bf16_float(best_scale);
-            for (int64_t k = 0; k < gw; ++k) out[k] = wq_code(wg[k], d);
+            if (fmt == ORC_FMT_TBL4_BF16G128) {
+                uint8_t *pk = (uint8_t *)codes + n * (K / 2) + g * (gw / 2);
+                for (int64_t c32 = 0; c32 < gw / 32; ++c32)
+                    for (int b = 0; b < 16; ++b)
+                        pk[16 * c32 + b] = (uint8_t)(tbl4_index(wg[32 * c32 + b], d) |
+                                                     (tbl4_index(wg[32 * c32 + 16 + b], d) << 4));
+            } else {
+                for (int64_t k = 0; k < gw; ++k) out[k] = wq_code(wg[k], d);
+            }
             if (fmt == ORC_FMT_U8G256_BF16ROW)
                 ((uint8_t *)gscale)[n * G + g] = (uint8_t)best_scale;
             else
@@ -547,7 +631,7 @@ int orc_rescore(const int8_t *qx, const float *s, const int8_t *qw, int fmt, con
         return ORC_E_ARG;
     if (fmt == ORC_FMT_U8G256_BF16ROW && !rscale) return ORC_E_ARG;
     int64_t G = K / gw;
-    if (G > 4096) return ORC_E_ARG;
+    if (G > 4096 || K > 65536) return ORC_E_ARG;
     size_t esz = (fmt == ORC_FMT_U8G256_BF16ROW) ? 1 : 2;
     int status = ORC_OK;
     #pragma omp parallel for collapse(2) schedule(static)
@@ -559,7 +643,8 @@ int orc_rescore(const int8_t *qx, const float *s, const int8_t *qw, int fmt, con
                 continue;
             }
             int32_t Prow[4096];
-            int rc = pair_partials(qx + m * K, qw + n * K, K, gw, Prow);
+            int8_t tmp[65536];
+            int rc = pair_partials(qx + m * K, weight_row(qw, fmt, n, K, tmp), K, gw, Prow);
             if (rc != ORC_OK) {
                 #pragma omp critical
                 status = rc;

@@ -100,7 +100,8 @@ def sizes(wl):
     from rotated_w8a8_int8_amd import workloads as W
     M, K, N, G = wl.M, wl.K, wl.N, wl.G
     esz = 1 if wl.fmt == W.FMT_U8G256_BF16ROW else 2
-    wbytes = N * K + N * G * esz + (N * 2 if wl.fmt == W.FMT_U8G256_BF16ROW else 0)
+    cbytes = N * K // 2 if wl.fmt == W.FMT_TBL4_BF16G128 else N * K      # packed 4-bit or int8 codes
+    wbytes = cbytes + N * G * esz + (N * 2 if wl.fmt == W.FMT_U8G256_BF16ROW else 0)
     return dict(
         weight=wbytes,
         step=M * K * 4 + wbytes + M * N * 4,                 # x, weights, y
@@ -394,7 +395,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
-                   "format": "u8g256_bf16row" if wl.fmt == W.FMT_U8G256_BF16ROW else "bf16g128",
+                   "format": {0: "u8g256_bf16row", 1: "bf16g128", 2: "tbl4_bf16g128"}[wl.fmt],
                    "weight_copies": ncopies, "launch": "eager" if args.eager else "hip_graph",
                    "host_ms_per_step": round(wall_ms_step, 5)},
         "roofline": roof,

@@ -62,7 +62,20 @@ enum rad_format {
     RAD_FMT_U8G256_BF16ROW = 0,
     /* Vocabulary head: codes int8 [N][K]; gscale bf16 bits [N][K/128];
        rscale must be NULL. */
-    RAD_FMT_BF16G128 = 1
+    RAD_FMT_BF16G128 = 1,
+    /* The drafter's linears (model card, table row "Speculator": a 16-level
+       integer codebook, four bits, in the same rotated domain; section "How
+       this file was made": rules with table=-127;-97;-75;-58;-43;-30;-18;-6;
+       6;18;30;43;58;75;97;127 group=128 scale=bf16 transform=fwht128):
+       codes are 4-bit indices into that table, packed uint8 [N][K/2] -- in
+       each 16-byte run of a row, byte b holds element 32c + b in its low
+       nibble and element 32c + 16 + b in its high nibble (c the run's index);
+       gscale bf16 bits [N][K/128]; rscale must be NULL.  The layer is the
+       head format applied to the table values.  Accepted by rad_w8a8_gemv,
+       rad_w8a8_gemm (which runs it through the M <= 128 kernels in chunks of
+       128 tokens), rad_w8a8_linear and rad_quant_weight_i8; not by
+       rad_w8a8_rescore. */
+    RAD_FMT_TBL4_BF16G128 = 2
 };
 
 /* Largest K that rad_quant_act_i8 accepts (its rows are held on chip). */
@@ -81,7 +94,7 @@ enum rad_format {
  * the end of either array).
  */
 typedef struct rad_w8a8_weight {
-    const int8_t *codes;     /* int8 [N][K]                                   */
+    const int8_t *codes;     /* int8 [N][K] (packed uint8 [N][K/2] for fmt 2)  */
     const void *gscale;      /* see enum rad_format                           */
     const uint16_t *rscale;  /* bf16 bits [N], or NULL for RAD_FMT_BF16G128    */
     int64_t N;               /* output features                               */
@@ -196,9 +209,10 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
  * calibration Hessians; this call is the round-to-nearest form.)
  *
  *   W       f32 [N][K] weights (unrotated), 16-byte aligned.
- *   codes   int8 [N][K] output, 16-byte aligned.
+ *   codes   int8 [N][K] output (packed 4-bit indices uint8 [N][K/2] for
+ *           RAD_FMT_TBL4_BF16G128), 16-byte aligned.
  *   gscale  output: uint8 [N][K/256] (RAD_FMT_U8G256_BF16ROW) or bf16 bits
- *           [N][K/128] (RAD_FMT_BF16G128), 4-byte aligned.
+ *           [N][K/128] (the other two formats), 4-byte aligned.
  *   rscale  output bf16 bits [N] for RAD_FMT_U8G256_BF16ROW (4-byte aligned);
  *           must be NULL for RAD_FMT_BF16G128.
  *   N >= 0; K > 0, K % group width == 0, K <= RAD_QUANT_WEIGHT_MAX_K.
@@ -210,6 +224,10 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
  *   RAD_FMT_U8G256_BF16ROW: r = bf16((amax_row / 127) / 255) with amax_row
  *     = max |w~| over the row, stored u8 = clamp(rne(t_c / r), 1, 255),
  *     d = r * u8 (r = 0, an all-zero row, stores u8 = 1 and zero codes).
+ *   RAD_FMT_TBL4_BF16G128: as the head format; each index picks the table
+ *     entry nearest to w~ / d (f32 division), a tie going to the entry of
+ *     smaller magnitude and 0 to +6 (d = 0: the index of +6); the error below
+ *     uses d * entry.
  * Codes are clamp(rne(w~ / d), -127, 127) (f32 division; d = 0 gives 0).  The
  * candidate with the least f64 sum of (w~ - d * code)^2 over the group wins
  * (the sum taken as a balanced pairwise tree in index order; ties go to the

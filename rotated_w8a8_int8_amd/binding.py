@@ -27,7 +27,8 @@ RAD_E_HIP = -7
 # enum rad_format
 RAD_FMT_U8G256_BF16ROW = 0
 RAD_FMT_BF16G128 = 1
-GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128}
+RAD_FMT_TBL4_BF16G128 = 2
+GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128, RAD_FMT_TBL4_BF16G128: 128}
 RAD_QUANT_MAX_K = 65536
 RAD_GEMV_MAX_M = 128
 RAD_QUANT_WEIGHT_MAX_K = 32768
@@ -121,7 +122,7 @@ def _stream(t):
 class W8A8Weight:
     """Device tensors of one quantised weight in the rotated domain.
 
-    codes  int8 [N][K]
+    codes  int8 [N][K] (RAD_FMT_TBL4_BF16G128: packed 4-bit indices uint8 [N][K/2])
     gscale uint8 [N][K/256] (RAD_FMT_U8G256_BF16ROW) or int16/uint16 bf16 bits [N][K/128]
     rscale int16/uint16 bf16 bits [N] for RAD_FMT_U8G256_BF16ROW, else None
     """
@@ -136,11 +137,11 @@ class W8A8Weight:
 
     @property
     def K(self) -> int:
-        return int(self.codes.shape[1])
+        return int(self.codes.shape[1]) * (2 if self.fmt == RAD_FMT_TBL4_BF16G128 else 1)
 
     def desc(self) -> WeightDesc:
         torch = _torch()
-        _dev(self.codes, torch.int8, "codes")
+        _dev(self.codes, torch.uint8 if self.fmt == RAD_FMT_TBL4_BF16G128 else torch.int8, "codes")
         if self.fmt == RAD_FMT_U8G256_BF16ROW:
             _dev(self.gscale, torch.uint8, "gscale")
         elif self.gscale.dtype not in (torch.int16, torch.uint16):
@@ -242,14 +243,16 @@ def quant_weight_i8(W, fmt: int, codes=None, gscale=None, rscale=None) -> W8A8We
     _dev(W, torch.float32, "W")
     N, K = W.shape
     G = K // GROUP_WIDTH[fmt]
+    tbl = fmt == RAD_FMT_TBL4_BF16G128
     if codes is None:
-        codes = torch.empty((N, K), dtype=torch.int8, device=W.device)
+        codes = torch.empty((N, K // 2 if tbl else K), dtype=torch.uint8 if tbl else torch.int8,
+                            device=W.device)
     if gscale is None:
         gdt = torch.uint8 if fmt == RAD_FMT_U8G256_BF16ROW else torch.int16
         gscale = torch.empty((N, G), dtype=gdt, device=W.device)
     if rscale is None and fmt == RAD_FMT_U8G256_BF16ROW:
         rscale = torch.empty((N,), dtype=torch.int16, device=W.device)
-    _dev(codes, torch.int8, "codes")
+    _dev(codes, torch.uint8 if tbl else torch.int8, "codes")
     if not (gscale.is_cuda and gscale.is_contiguous()):
         raise TypeError("gscale must be a contiguous GPU tensor")
     if rscale is not None and not (rscale.is_cuda and rscale.is_contiguous()):

@@ -33,6 +33,7 @@ namespace rad {
 namespace {
 
 constexpr int kFmtU8 = 0;
+constexpr int kFmtTbl4 = 2;
 constexpr int kBM = 256, kBN = 128, kKC = 128;
 constexpr int kWavesM = 4, kWavesN = 2;        // 8 waves, two per SIMD
 constexpr int kWaves = kWavesM * kWavesN;
@@ -368,9 +369,11 @@ hipError_t launch_gemm_t(const int8_t *q, const float *s, const WeightArgs &w, f
 hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st) {
     const int64_t scale_bytes = w.N * (w.K / (w.fmt == kFmtU8 ? 256 : 128)) * (w.fmt == kFmtU8 ? 1 : 2);
-    if (scale_bytes < 4) {
-        // too few group scales for the kernel's dword scale loads: run the
-        // batch through the M <= 128 path, 128 tokens at a time
+    if (scale_bytes < 4 || w.fmt == kFmtTbl4) {
+        // too few group scales for the kernel's dword scale loads, or the
+        // drafter's 4-bit codebook (expanded in registers by the M <= 128
+        // kernels only): run the batch through the M <= 128 path, 128
+        // tokens at a time
         const int64_t G = w.K / (w.fmt == kFmtU8 ? 256 : 128);
         for (int64_t m0 = 0; m0 < M; m0 += 128) {
             const int64_t mc = M - m0 < 128 ? M - m0 : 128;

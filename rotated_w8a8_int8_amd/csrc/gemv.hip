@@ -30,6 +30,10 @@ namespace {
 
 constexpr int kFmtU8 = 0;
 constexpr int kFmtHead = 1;
+constexpr int kFmtTbl4 = 2;    // 4-bit codebook indices, packed two per byte
+
+// K elements held by one byte of a weight row
+template <int FMT> constexpr int kElemsPerByte = (FMT == kFmtTbl4) ? 2 : 1;
 
 // ------------------------------------------------------------- M == 1 ----
 // Layout: a wave streams 4 weight rows at a time (a "quad"), one 16-lane DPP
@@ -52,6 +56,12 @@ constexpr int kFmtHead = 1;
 // FUSED: the workgroup first rotates and quantises the f32 token itself (the
 // same device code and bits as rad_quant_act_i8) while its first weight loads
 // are in flight; block 0 also writes the codes and the scale out.
+//
+// Codebook format: a row is K / 2 bytes of packed indices, so a 16-byte load
+// holds 32 elements (a "run": low nibbles elements 0..15, high nibbles 16..31)
+// and step t covers 512 elements of the row; each lane expands its run to
+// int8 table values in registers (v_perm lookups) and dots them with 32
+// activation codes.  Four lanes make one 128-element group.
 constexpr int kScBytes = 2048;   // per-wave LDS staging of group scales
 constexpr int kRsBytes = 128;    // per-wave LDS staging of row scales (16 quads)
 constexpr int kM1MaxK = 20480;   // K handled by the one-token path
@@ -65,13 +75,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
                                                      const uint16_t *__restrict__ rscale,
                                                      float *__restrict__ y,
                                                      int32_t *__restrict__ partials, int N, int K) {
-    constexpr int GW16 = (FMT == kFmtU8) ? 16 : 8;    // 16-byte chunks per group
+    constexpr int EPB = kElemsPerByte<FMT>;
+    constexpr int GW16 = (FMT == kFmtU8) ? 16 : (FMT == kFmtHead ? 8 : 4);   // 16-byte chunks per group
     constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;      // bytes per group scale
     constexpr int SP = ((STEPS + D - 1) / D) * D;     // steps per quad incl. padding
-    constexpr int NQ = (STEPS + 7) / 8;               // 16-block rotation steps (K <= 256 STEPS)
+    constexpr int KSTEP = 256 * EPB;                  // K elements per step
+    constexpr int NQ = (STEPS * KSTEP / 128 + 15) / 16;   // 16-block rotation steps
     __shared__ __attribute__((aligned(16))) uint8_t sc_lds[4][kScBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rs_lds[4][kRsBytes];
-    __shared__ __attribute__((aligned(16))) int8_t q_lds[STEPS * 256];
+    __shared__ __attribute__((aligned(16))) int8_t q_lds[STEPS * KSTEP];
     __shared__ float red[4];
 
     const int lane = threadIdx.x & 63;
@@ -82,7 +94,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
     const int W = gridDim.x * 4;
     const int nq = (N + 3) >> 2;
     const int cnt = wave < nq ? (nq - wave + W - 1) / W : 0;   // quads of this wave
-    const int nchunk = K >> 4;
+    const int RB = K / EPB;                            // bytes of a weight row
+    const int nchunk = RB >> 4;
     const int G = nchunk / GW16;
     const int qsb = 4 * G * ESZ;                       // scale bytes of one quad (multiple of 4)
     const int64_t allsb = static_cast<int64_t>(N) * G * ESZ;
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
     auto row_ptr = [&](int i) -> const int8_t * {
         const int ii = min(i, cnt - 1);
         const int row = min(4 * (wave + ii * W) + r4, N - 1);
-        return codes + static_cast<int64_t>(row) * K + 16 * l16;
+        return codes + static_cast<int64_t>(row) * RB + 16 * l16;
     };
     auto wload = [&](const int8_t *rp, int t) -> v4i {
         if (t >= STEPS) return v4i{0, 0, 0, 0};       // padding step: no load
@@ -221,8 +234,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
         for (int t = 0; t < SP; ++t) {
             if (t < STEPS) {
                 const int c = l16 + 16 * t;
-                const v4i av = *reinterpret_cast<const v4i *>(&q_lds[16 * c + qoff]);
-                const int p = dot16_i8(ring[t % D], av, 0);
+                int p;
+                if constexpr (FMT == kFmtTbl4) {
+                    v4i lo, hi;
+                    tbl4_decode16(ring[t % D], lo, hi);
+                    const v4i a0 = *reinterpret_cast<const v4i *>(&q_lds[32 * c + qoff]);
+                    const v4i a1 = *reinterpret_cast<const v4i *>(&q_lds[32 * c + 16 + qoff]);
+                    p = dot16_i8(hi, a1, dot16_i8(lo, a0, 0));
+                } else {
+                    const v4i av = *reinterpret_cast<const v4i *>(&q_lds[16 * c + qoff]);
+                    p = dot16_i8(ring[t % D], av, 0);
+                }
                 if constexpr (FMT == kFmtU8) {
                     const int prod = p * static_cast<int>(scq[t]);     // |prod| < 2^26
                     if constexpr (STEPS <= 32) {
@@ -236,12 +258,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
                         if (l16 == 0 && row < N) partials[static_cast<int64_t>(row) * G + t] = pg;
                     }
                 } else if (c < nchunk) {
-                    const int g = 2 * t + (l16 >> 3);
+                    const int g = c / GW16;                    // GW16 lanes make a group
                     const uint16_t b = *reinterpret_cast<const uint16_t *>(&scq[2 * g]);
                     accf += static_cast<float>(p) * bf16_to_f32(b);
                     if constexpr (WRITE_P) {
-                        const int pg = row8_sum(p);
-                        if ((l16 & 7) == 0 && row < N) partials[static_cast<int64_t>(row) * G + g] = pg;
+                        const int pg = (GW16 == 8) ? row8_sum(p) : row4_sum(p);
+                        if ((l16 % GW16) == 0 && row < N) partials[static_cast<int64_t>(row) * G + g] = pg;
                     }
                 }
             }
@@ -278,7 +300,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
 
 // Quads per wave: about TARGET waves in all, bounded by the LDS staging.
 inline int decode_quads_per_wave(int64_t N, int64_t K, int fmt, int target_waves) {
-    const int G = static_cast<int>(K / (fmt == kFmtU8 ? 256 : 128));
+    const int G = static_cast<int>(K / (fmt == kFmtU8 ? 256 : 128));   // head and codebook: 128
     const int esz = fmt == kFmtU8 ? 1 : 2;
     const int nq = static_cast<int>((N + 3) / 4);
     int qpw = (nq + target_waves - 1) / target_waves;
@@ -310,8 +332,12 @@ hipError_t launch_m1_t(const float *x, int8_t *q, float *s, const WeightArgs &w,
 #define RAD_M1_STEPS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(14) \
     X(16) X(20) X(24) X(28) X(32) X(40) X(48) X(56) X(64) X(68) X(72) X(80)
 
-inline bool m1_steps_supported(int64_t K) {
-    const int steps = static_cast<int>((K + 255) / 256);
+// steps of the one-token kernel: 256 bytes of a weight row each
+inline int m1_steps(int64_t K, int fmt) {
+    return static_cast<int>((K + 256 * (fmt == kFmtTbl4 ? 2 : 1) - 1) / (256 * (fmt == kFmtTbl4 ? 2 : 1)));
+}
+
+inline bool m1_steps_supported(int steps) {
     switch (steps) {
 #define RAD_M1_YES(S) case S: return true;
         RAD_M1_STEPS(RAD_M1_YES)
@@ -323,8 +349,7 @@ inline bool m1_steps_supported(int64_t K) {
 template <int FMT, bool FUSED>
 hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y, int32_t *P,
                      hipStream_t st) {
-    const int steps = static_cast<int>((w.K + 255) / 256);
-    switch (steps) {
+    switch (m1_steps(w.K, FMT)) {
 #define RAD_M1_CASE(S) case S: return launch_m1_t<FMT, S, FUSED>(x, q, s, w, y, P, st);
         RAD_M1_STEPS(RAD_M1_CASE)
 #undef RAD_M1_CASE
@@ -356,6 +381,13 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 // MFMA sums exactly the 64 products of its k-step; P[mb] element e is token
 // 16 mb + 4 q + e, row n0 + j.  Each K group's partials are folded into f32
 // with the group scale once the group's stages are done.
+//
+// Codebook format: a stage of a weight row is 64 bytes of packed indices;
+// lane j + 16 q loads the 16-byte run q (elements 32 q .. 32 q + 31 of the
+// stage), expands it in registers, and uses its first 16 values in k-step 0
+// and the other 16 in k-step 1.  The A operand follows the same assignment
+// (token bytes 32 q + 16 kk of the stage), which keeps every product inside
+// the stage, i.e. inside its 128-element group.
 //
 // LDS: token row m of a stage occupies 128 bytes, its 16-byte chunk c stored
 // in slot c ^ (m mod 8).  With the 16x16x64 operand layout (lane j + 16 q
@@ -444,12 +476,14 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
     const int nrow = n0 + j;
     const bool nvalid = nrow < N;
     const int nr = min(nrow, N - 1);
-    const int8_t *wrow = codes + static_cast<int64_t>(nr) * K + 16 * qd;
+    constexpr int EPB = kElemsPerByte<FMT>;
+    constexpr int WL = 2 / EPB;                       // 16-byte weight loads per stage
+    const int8_t *wrow = codes + static_cast<int64_t>(nr) * (K / EPB) + 16 * qd;
 
-    auto load_w = [&](int s, v4i(&dst)[2]) {
-        const int64_t off = static_cast<int64_t>(phys(s)) * kSkStageK;
+    auto load_w = [&](int s, v4i(&dst)[WL]) {
+        const int64_t off = static_cast<int64_t>(phys(s)) * (kSkStageK / EPB);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) dst[kk] = ld16(wrow + off + 64 * kk);
+        for (int kk = 0; kk < WL; ++kk) dst[kk] = ld16(wrow + off + 64 * kk);
     };
     // Group scales ride in the ring as raw bits and are converted only when
     // folded: converting at load time would make the wave wait for the load
@@ -468,7 +502,7 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
             return bf16_to_f32(static_cast<uint16_t>(raw));
     };
 
-    v4i wr[kSkD][2];
+    v4i wr[kSkD][WL];
     uint32_t scr[kSkD / SPG];                         // scale bits of each group in the ring
 #pragma unroll
     for (int i = 0; i < kSkD; ++i) {
@@ -497,14 +531,22 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
         __builtin_amdgcn_s_barrier();                 // stage s is in LDS
         asm volatile("" ::: "memory");
         const int8_t *Ab = As[s % kSkRing];
+        v4i bw[2];                                    // the stage's B operands
+        if constexpr (FMT == kFmtTbl4) {
+            tbl4_decode16(wr[i][0], bw[0], bw[1]);
+        } else {
+            bw[0] = wr[i][0];
+            bw[1] = wr[i][1];
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             v4i a[MB];                                // the k-step's A fragments, read together
+            const int ac = (FMT == kFmtTbl4) ? 2 * qd + kk : 4 * kk + qd;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + a_off(mb, 4 * kk + qd));
+            for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + a_off(mb, ac));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb], wr[i][kk], P[mb], 0, 0, 0);
+                P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb], bw[kk], P[mb], 0, 0, 0);
         }
         load_w(s + kSkD, wr[i]);                      // refill the slot just used
         if (i % SPG == SPG - 1) {
@@ -585,7 +627,7 @@ hipError_t launch_skinny(const int8_t *q, const float *s, const WeightArgs &w, f
 inline bool m1_supported(int64_t K, int fmt) {
     const int G = static_cast<int>(K / (fmt == kFmtU8 ? 256 : 128));
     const int esz = fmt == kFmtU8 ? 1 : 2;
-    return K <= kM1MaxK && 4 * G * esz <= kScBytes && m1_steps_supported(K);
+    return K <= kM1MaxK && 4 * G * esz <= kScBytes && m1_steps_supported(m1_steps(K, fmt));
 }
 
 }  // namespace
@@ -595,19 +637,22 @@ hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, flo
     if (M == 1 && m1_supported(w.K, w.fmt)) {
         int8_t *qi = const_cast<int8_t *>(q);            // read only: FUSED == false
         float *si = const_cast<float *>(s);
-        return w.fmt == kFmtU8 ? launch_m1<kFmtU8, false>(nullptr, qi, si, w, y, partials, st)
-                               : launch_m1<kFmtHead, false>(nullptr, qi, si, w, y, partials, st);
+        if (w.fmt == kFmtU8) return launch_m1<kFmtU8, false>(nullptr, qi, si, w, y, partials, st);
+        if (w.fmt == kFmtHead) return launch_m1<kFmtHead, false>(nullptr, qi, si, w, y, partials, st);
+        return launch_m1<kFmtTbl4, false>(nullptr, qi, si, w, y, partials, st);
     }
-    return w.fmt == kFmtU8 ? launch_skinny<kFmtU8>(q, s, w, y, M, partials, st)
-                           : launch_skinny<kFmtHead>(q, s, w, y, M, partials, st);
+    if (w.fmt == kFmtU8) return launch_skinny<kFmtU8>(q, s, w, y, M, partials, st);
+    if (w.fmt == kFmtHead) return launch_skinny<kFmtHead>(q, s, w, y, M, partials, st);
+    return launch_skinny<kFmtTbl4>(q, s, w, y, M, partials, st);
 }
 
 bool fused_decode_supported(const WeightArgs &w, int64_t M) { return M == 1 && m1_supported(w.K, w.fmt); }
 
 hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
                                hipStream_t st) {
-    return w.fmt == kFmtU8 ? launch_m1<kFmtU8, true>(x, q, s, w, y, nullptr, st)
-                           : launch_m1<kFmtHead, true>(x, q, s, w, y, nullptr, st);
+    if (w.fmt == kFmtU8) return launch_m1<kFmtU8, true>(x, q, s, w, y, nullptr, st);
+    if (w.fmt == kFmtHead) return launch_m1<kFmtHead, true>(x, q, s, w, y, nullptr, st);
+    return launch_m1<kFmtTbl4, true>(x, q, s, w, y, nullptr, st);
 }
 
 }  // namespace rad

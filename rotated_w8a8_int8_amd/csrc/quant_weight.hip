@@ -19,6 +19,12 @@
 //   error: sum over the group of (w~ - d q)^2 in f64, the sum taken as the
 //        balanced pairwise tree over the group in index order;
 //   the least error wins, ties to the smaller c.
+// The drafter's codebook format (group 128, bf16 scale, model card "Qwen3.8-27B
+// IQ8R + DFlash2 -- radiance container", section "How this file was made",
+// rules dflash.*: rtn table=... rule=search) uses the head format's candidates;
+// a code is the index of the table entry nearest to w~ / d (f32 division), a
+// tie going to the smaller magnitude and 0 to +6, and the error uses d times
+// that entry.  Its codes are always taken through the division.
 //
 // Layout: one 256-thread workgroup per weight row.  Phase 1 rotates the row
 // block by block (16 lanes per block, butterflies in registers and DPP) into
@@ -38,7 +44,27 @@ namespace rad {
 namespace {
 
 constexpr int kFmtU8 = 0;
+constexpr int kFmtTbl4 = 2;
 constexpr int kWqCandidates = 16;
+
+// Nearest codebook entry to w / d: index (0..15) and value.  |t| is compared
+// with the midpoints between the positive entries 6, 18, 30, 43, 58, 75, 97,
+// 127 (all exact in f32); equality keeps the inner entry.
+__device__ __forceinline__ int tbl4_nearest(float w, float d, float &value) {
+    if (d == 0.0f) {
+        value = 6.0f;
+        return 8;
+    }
+    const float t = w / d;
+    const float a = fabsf(t);
+    const int cnt = (a > 12.0f) + (a > 24.0f) + (a > 36.5f) + (a > 50.5f) + (a > 66.5f) + (a > 86.0f) +
+                    (a > 112.0f);
+    const uint32_t mag = __builtin_amdgcn_perm(tbl4_dword(58, 75, 97, 127), tbl4_dword(6, 18, 30, 43),
+                                               static_cast<uint32_t>(cnt)) & 0xFFu;
+    const bool pos = t >= 0.0f;
+    value = pos ? static_cast<float>(mag) : -static_cast<float>(mag);
+    return pos ? 8 + cnt : 7 - cnt;
+}
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -102,6 +128,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
                                                            uint16_t *__restrict__ rscale, int K) {
     constexpr int GW = (FMT == kFmtU8) ? 256 : 128;
     constexpr int LEVELS = (FMT == kFmtU8) ? 6 : 5;       // lanes per group = 2^LEVELS
+    constexpr int CB = (FMT == kFmtTbl4) ? 2 : 1;         // K elements per code byte
     extern __shared__ __attribute__((aligned(16))) float qw_lds[];
     float *wt = qw_lds;
     float *bamax = qw_lds + K + 128;
@@ -177,6 +204,22 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
                 stored = bf16_rne(target);
                 d = bf16_to_f32(static_cast<uint16_t>(stored));
             }
+            if constexpr (FMT == kFmtTbl4) {
+                float v0, v1, v2, v3;
+                tbl4_nearest(w.x, d, v0);
+                tbl4_nearest(w.y, d, v1);
+                tbl4_nearest(w.z, d, v2);
+                tbl4_nearest(w.w, d, v3);
+                const double s01 = __dadd_rn(wq_sq(w.x, d, v0), wq_sq(w.y, d, v1));
+                const double s23 = __dadd_rn(wq_sq(w.z, d, v2), wq_sq(w.w, d, v3));
+                const double err = tree_sum<LEVELS>(__dadd_rn(s01, s23));
+                if (c == 0 || err < best_err) {
+                    best_err = err;
+                    best_d = d;
+                    best_stored = stored;
+                }
+                continue;
+            }
             // codes: through the reciprocal where that provably rounds alike,
             // else (any lane of the wave near a half-integer, or d outside
             // the normal range) through the division for the whole wave
@@ -200,6 +243,24 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
                 best_d = d;
                 best_stored = stored;
             }
+        }
+        if constexpr (FMT == kFmtTbl4) {
+            // lane i holds elements 4i..4i+3 of the span: run i / 8, low
+            // nibbles if i % 8 < 4, else high nibbles of the same 4 bytes as
+            // lane i - 4; the low lane gathers both and stores the dword
+            float v;
+            const uint32_t ix = static_cast<uint32_t>(tbl4_nearest(w.x, best_d, v)) |
+                                (static_cast<uint32_t>(tbl4_nearest(w.y, best_d, v)) << 8) |
+                                (static_cast<uint32_t>(tbl4_nearest(w.z, best_d, v)) << 16) |
+                                (static_cast<uint32_t>(tbl4_nearest(w.w, best_d, v)) << 24);
+            const uint32_t other = static_cast<uint32_t>(lane_xor<4>(static_cast<int>(ix)));
+            if (g < G && (lane & 4) == 0) {
+                *reinterpret_cast<uint32_t *>(codes + static_cast<int64_t>(n) * (K / CB) + sp * 128 +
+                                              16 * (lane >> 3) + 4 * (lane & 3)) = ix | (other << 4);
+                if ((lane & 31) == 0)
+                    static_cast<uint16_t *>(gscale)[static_cast<int64_t>(n) * G + g] = static_cast<uint16_t>(best_stored);
+            }
+            continue;
         }
         const uint32_t b0 = static_cast<uint32_t>(static_cast<int>(wq_code(w.x, best_d))) & 0xFFu;
         const uint32_t b1 = static_cast<uint32_t>(static_cast<int>(wq_code(w.y, best_d))) & 0xFFu;
@@ -236,8 +297,9 @@ hipError_t launch_qw(const float *W, int8_t *codes, void *gscale, uint16_t *rsca
 
 hipError_t launch_quant_weight(const float *W, int8_t *codes, void *gscale, uint16_t *rscale,
                                int64_t N, int64_t K, int fmt, hipStream_t st) {
-    return fmt == kFmtU8 ? launch_qw<0>(W, codes, gscale, rscale, N, K, st)
-                         : launch_qw<1>(W, codes, gscale, rscale, N, K, st);
+    if (fmt == kFmtU8) return launch_qw<0>(W, codes, gscale, rscale, N, K, st);
+    if (fmt == kFmtTbl4) return launch_qw<2>(W, codes, gscale, rscale, N, K, st);
+    return launch_qw<1>(W, codes, gscale, rscale, N, K, st);
 }
 
 }  // namespace rad

@@ -27,9 +27,11 @@ static_assert(RAD_QUANT_WEIGHT_MAX_K == rad::kQuantWeightMaxK, "header and kerne
 
 int group_width(int32_t fmt) {
     if (fmt == RAD_FMT_U8G256_BF16ROW) return 256;
-    if (fmt == RAD_FMT_BF16G128) return 128;
+    if (fmt == RAD_FMT_BF16G128 || fmt == RAD_FMT_TBL4_BF16G128) return 128;
     return 0;
 }
+// bytes of weight codes per row
+int64_t code_bytes(int32_t fmt, int64_t K) { return fmt == RAD_FMT_TBL4_BF16G128 ? K / 2 : K; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RAD_OK : RAD_E_HIP; }
 
@@ -40,7 +42,7 @@ int check_linear(const int8_t *q, const float *scale, const rad_w8a8_weight *w, 
     const int gw = group_width(w->fmt);
     if (gw == 0) return RAD_E_FMT;
     if (w->fmt == RAD_FMT_U8G256_BF16ROW && !w->rscale) return RAD_E_FMT;
-    if (w->fmt == RAD_FMT_BF16G128 && w->rscale) return RAD_E_FMT;
+    if (w->fmt != RAD_FMT_U8G256_BF16ROW && w->rscale) return RAD_E_FMT;
     if (M < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
     if (M > max_m || w->N > kI32Max || w->K > kI32Max) return RAD_E_RANGE;
     if (M == 0 || w->N == 0) return 1;  // nothing to do
@@ -51,7 +53,7 @@ int check_linear(const int8_t *q, const float *scale, const rad_w8a8_weight *w, 
         return RAD_E_ALIGN;
     const int64_t N = w->N, K = w->K, G = K / gw;
     const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
-    const Span in[] = {span(q, M * K), span(scale, M * 4), span(w->codes, N * K),
+    const Span in[] = {span(q, M * K), span(scale, M * 4), span(w->codes, N * code_bytes(w->fmt, K)),
                        span(w->gscale, N * G * esz),
                        w->rscale ? span(w->rscale, N * 2) : Span{0, 0}};
     const Span ys = span(y, M * N * 4);
@@ -123,7 +125,7 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
     const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
     const Span xs = span(x, M * K * 4), qs = span(q, M * K), ss = span(scale, M * 4),
                ys = span(y, M * N * 4);
-    const Span ws[] = {span(w->codes, N * K), span(w->gscale, N * (K / gw) * esz),
+    const Span ws[] = {span(w->codes, N * code_bytes(w->fmt, K)), span(w->gscale, N * (K / gw) * esz),
                        w->rscale ? span(w->rscale, N * 2) : Span{0, 0}};
     if (overlap(xs, qs) || overlap(xs, ss) || overlap(qs, ss) || overlap(xs, ys)) return RAD_E_ALIAS;
     for (const Span &o : ws)
@@ -143,7 +145,7 @@ int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
     const int gw = group_width(fmt);
     if (gw == 0) return RAD_E_FMT;
     if (fmt == RAD_FMT_U8G256_BF16ROW && !rscale) return RAD_E_FMT;
-    if (fmt == RAD_FMT_BF16G128 && rscale) return RAD_E_FMT;
+    if (fmt != RAD_FMT_U8G256_BF16ROW && rscale) return RAD_E_FMT;
     if (N < 0 || K <= 0 || K % 128 != 0 || K % gw != 0) return RAD_E_SHAPE;
     if (K > RAD_QUANT_WEIGHT_MAX_K || N > kI32Max) return RAD_E_RANGE;
     if (N == 0) return RAD_OK;
@@ -151,7 +153,8 @@ int rad_quant_weight_i8(const float *W, int8_t *codes, void *gscale, uint16_t *r
     if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(gscale, 4) || (rscale && !aligned(rscale, 4)))
         return RAD_E_ALIGN;
     const int esz = (fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
-    const Span ws = span(W, N * K * 4), cs = span(codes, N * K), gs = span(gscale, N * (K / gw) * esz),
+    const Span ws = span(W, N * K * 4), cs = span(codes, N * code_bytes(fmt, K)),
+               gs = span(gscale, N * (K / gw) * esz),
                rs = rscale ? span(rscale, N * 2) : Span{0, 0};
     if (overlap(ws, cs) || overlap(ws, gs) || overlap(ws, rs) || overlap(cs, gs) || overlap(cs, rs) ||
         overlap(gs, rs))
@@ -166,7 +169,8 @@ int rad_w8a8_rescore(const int8_t *q, const float *scale, const rad_w8a8_weight 
     const int gw = group_width(w->fmt);
     if (gw == 0) return RAD_E_FMT;
     if (w->fmt == RAD_FMT_U8G256_BF16ROW && !w->rscale) return RAD_E_FMT;
-    if (w->fmt == RAD_FMT_BF16G128 && w->rscale) return RAD_E_FMT;
+    if (w->fmt != RAD_FMT_U8G256_BF16ROW && w->rscale) return RAD_E_FMT;
+    if (w->fmt == RAD_FMT_TBL4_BF16G128) return RAD_E_FMT;       // int8 weights only
     if (M < 0 || C < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
     if (w->N > kI32Max || w->K > kI32Max || C > kI32Max || M > kI32Max || M * C >= (int64_t(1) << 33))
         return RAD_E_RANGE;

@@ -78,6 +78,13 @@ __device__ __forceinline__ int row8_sum(int v) {
     return v;
 }
 
+// Exact integer sum over each aligned group of 4 lanes.
+__device__ __forceinline__ int row4_sum(int v) {
+    v += lane_xor<1>(v);
+    v += lane_xor<2>(v);
+    return v;
+}
+
 // Wave-uniform sum of an int over all 64 lanes (result in a scalar register).
 __device__ __forceinline__ int wave_sum_i32(int v) {
     v = row16_sum(v);
@@ -176,6 +183,42 @@ __device__ __forceinline__ void dma4(const void *sbase, uint32_t voff, uint32_t 
         : "v"(voff), "s"(sbase), "{m0}"(lds)
         : "memory");
 }
+// ---- the drafter's 16-level codebook (4-bit indices) ----------------------
+// Values as printed in the recipe rules of section "How this file was made" on
+// the model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance container" (rules
+// dflash.*: rtn table=-127;-97;-75;-58;-43;-30;-18;-6;6;18;30;43;58;75;97;127).
+constexpr uint32_t tbl4_dword(int a, int b, int c, int d) {
+    return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
+           ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+}
+constexpr uint32_t kTbl4_0 = tbl4_dword(-127, -97, -75, -58);
+constexpr uint32_t kTbl4_1 = tbl4_dword(-43, -30, -18, -6);
+constexpr uint32_t kTbl4_2 = tbl4_dword(6, 18, 30, 43);
+constexpr uint32_t kTbl4_3 = tbl4_dword(58, 75, 97, 127);
+
+// Four indices (one in the low nibble of each byte of n, high nibbles zero)
+// -> their four int8 table values, in the same byte order.  v_perm picks byte
+// (index mod 8) from the lower or the upper half of the table, bit 3 of the
+// index chooses the half.
+__device__ __forceinline__ uint32_t tbl4_lookup4(uint32_t n) {
+    const uint32_t sel = n & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(kTbl4_1, kTbl4_0, sel);   // entries 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(kTbl4_3, kTbl4_2, sel);   // entries 8..15
+    const uint32_t m = ((n >> 3) & 0x01010101u) * 0xFFu;
+    return (hi & m) | (lo & ~m);
+}
+// One 16-byte run of packed indices (32 elements: byte b holds element b in
+// its low nibble and element 16 + b in its high nibble) -> the int8 values of
+// elements 0..15 (lo) and 16..31 (hi).
+__device__ __forceinline__ void tbl4_decode16(v4i packed, v4i &lo, v4i &hi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w = static_cast<uint32_t>(packed[i]);
+        lo[i] = static_cast<int>(tbl4_lookup4(w & 0x0F0F0F0Fu));
+        hi[i] = static_cast<int>(tbl4_lookup4((w >> 4) & 0x0F0F0F0Fu));
+    }
+}
+
 // LDS byte offset of a __shared__ object (the low half of its flat address).
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));

@@ -9,11 +9,11 @@
 namespace rad {
 
 struct WeightArgs {
-    const int8_t *codes;     // int8 [N][K]
+    const int8_t *codes;     // int8 [N][K], or packed 4-bit indices [N][K/2] (fmt 2)
     const void *gscale;      // u8 [N][K/256] or bf16 bits [N][K/128]
     const uint16_t *rscale;  // bf16 bits [N] (u8 format) or nullptr
     int64_t N, K;
-    int fmt;                 // 0: u8 per 256 + bf16 row; 1: bf16 per 128
+    int fmt;                 // 0: u8 per 256 + bf16 row; 1: bf16 per 128; 2: codebook, bf16 per 128
 };
 
 hipError_t launch_fwht128(const float *x, float *y, int64_t rows, int64_t K, hipStream_t st);

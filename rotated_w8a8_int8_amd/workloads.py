@@ -19,15 +19,23 @@ decode_gate_up     1       5120   34816   one decode token, fused gate_up
 verify_skinny      128     5120   34816   8 sequences x 16-token draft block
 prefill_down       8192    17408  5120    8K-token prefill, down projection
 vocab_head         64      5120   152064  head, bf16 scale per (row, 128 K)
+drafter_decode     1       5120   34816   4-bit codebook linear, one token
+drafter_block      16      5120   34816   4-bit codebook linear, 16-token block
 =================  ======  =====  ======  ===================================
+
+The drafter workloads use the drafter's 4-bit codebook format on a weight of
+the trunk's gate_up shape (the drafter's own dimensions are not given); its
+16-token block is the draft block of a speculative step.
 
 Draw order per workload, one ``numpy.random.Generator(PCG64(seed))``:
 
 1. x = standard_normal((M, K), float32)
 2. mask = random((M, K)) < 0.01; x[mask] *= 20        (1% outliers x20)
 3. q_w = integers(-127, 127, (N, K), int8, endpoint=True)
+   codebook format: packed = integers(0, 255, (N, K/2), uint8, endpoint=True)
+   (two uniform 4-bit indices per byte)
 4. u8 format: u8 = integers(1, 255, (N, K/256), uint8, endpoint=True)
-   head format: b = bf16(uniform(1e-4, 1e-3, (N, K/128)))
+   head and codebook formats: b = bf16(uniform(1e-4, 1e-3, (N, K/128)))
 5. u8 format only: r = bf16(uniform(1e-4, 1e-3, N))
 
 bf16(v): v (f64) is cast to f32, then rounded to the nearest bf16, ties to
@@ -41,7 +49,8 @@ import numpy as np
 
 FMT_U8G256_BF16ROW = 0
 FMT_BF16G128 = 1
-GROUP_WIDTH = {FMT_U8G256_BF16ROW: 256, FMT_BF16G128: 128}
+FMT_TBL4_BF16G128 = 2
+GROUP_WIDTH = {FMT_U8G256_BF16ROW: 256, FMT_BF16G128: 128, FMT_TBL4_BF16G128: 128}
 
 
 @dataclass(frozen=True)
@@ -70,6 +79,10 @@ WORKLOADS = {
                  "prefill GEMM, down projection"),
         Workload("vocab_head", 64, 5120, 152064, FMT_BF16G128,
                  "vocabulary head, bf16 scale per (row, 128 of K)"),
+        Workload("drafter_decode", 1, 5120, 34816, FMT_TBL4_BF16G128,
+                 "drafter linear on the 4-bit codebook, one token"),
+        Workload("drafter_block", 16, 5120, 34816, FMT_TBL4_BF16G128,
+                 "drafter linear on the 4-bit codebook, 16-token draft block"),
     )
 }
 ORDER = ["tiny", "decode_gate_up", "verify_skinny", "prefill_down", "vocab_head"]
@@ -89,7 +102,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 @dataclass
 class Inputs:
     x: np.ndarray          # f32 [M][K]
-    qw: np.ndarray         # int8 [N][K], rotated domain
+    qw: np.ndarray         # int8 [N][K], rotated domain (codebook: packed uint8 [N][K/2])
     gscale: np.ndarray     # uint8 [N][K/256] or uint16 (bf16 bits) [N][K/128]
     rscale: np.ndarray | None  # uint16 (bf16 bits) [N] or None
     fmt: int
@@ -104,7 +117,10 @@ def make(M: int, K: int, N: int, fmt: int = FMT_U8G256_BF16ROW, seed: int = 0,
     x = rng.standard_normal((M, K), dtype=np.float32)
     mask = rng.random((M, K)) < outlier_frac
     x[mask] *= np.float32(outlier_mul)
-    qw = rng.integers(-127, 127, size=(N, K), dtype=np.int8, endpoint=True)
+    if fmt == FMT_TBL4_BF16G128:
+        qw = rng.integers(0, 255, size=(N, K // 2), dtype=np.uint8, endpoint=True)
+    else:
+        qw = rng.integers(-127, 127, size=(N, K), dtype=np.int8, endpoint=True)
     if fmt == FMT_U8G256_BF16ROW:
         gscale = rng.integers(1, 255, size=(N, K // gw), dtype=np.uint8, endpoint=True)
         rscale = f32_to_bf16_bits(rng.uniform(1e-4, 1e-3, size=N).astype(np.float32))

@@ -43,7 +43,7 @@ def test_constants_match_header():
     h = header_text()
     for name in ("RAD_OK", "RAD_E_NULL", "RAD_E_SHAPE", "RAD_E_ALIGN", "RAD_E_FMT",
                  "RAD_E_RANGE", "RAD_E_ALIAS", "RAD_E_HIP", "RAD_FMT_U8G256_BF16ROW",
-                 "RAD_FMT_BF16G128"):
+                 "RAD_FMT_BF16G128", "RAD_FMT_TBL4_BF16G128"):
         m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, h)
         assert m and int(m.group(1)) == getattr(B, name), name
     for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M", "RAD_QUANT_WEIGHT_MAX_K"):
@@ -223,3 +223,19 @@ def test_rescore_validation():
     assert call(desc(), ids=E2 + 2) == B.RAD_E_ALIGN
     assert call(desc(), y=E2 + 64) == B.RAD_E_ALIAS                 # y over ids
     assert call(desc(), y=C + 128) == B.RAD_E_ALIAS                 # y over codes
+
+
+def test_codebook_format_validation():
+    TBL = B.RAD_FMT_TBL4_BF16G128
+    f = B.lib().rad_w8a8_gemv
+    d = desc(fmt=TBL, rscale=None, K=512)
+    assert f(A, Bp, ctypes.byref(desc(fmt=TBL, K=512)), F, 4, None, None) == B.RAD_E_FMT    # no row scales
+    assert f(A, Bp, ctypes.byref(desc(fmt=TBL, rscale=None, K=200)), F, 4, None, None) == B.RAD_E_SHAPE
+    # packed codes span N*K/2 bytes (a call that passes every check would
+    # launch, so only failing calls are made here)
+    assert f(A, Bp, ctypes.byref(d), C + 64 * 256 - 256, 4, None, None) == B.RAD_E_ALIAS
+    r = B.lib().rad_w8a8_rescore
+    assert r(A, Bp, ctypes.byref(d), E, 32, F, 4, None) == B.RAD_E_FMT                    # not supported
+    q = B.lib().rad_quant_weight_i8
+    assert q(A, Bp, C, D, 4, 512, TBL, None) == B.RAD_E_FMT                               # no row scales
+    assert q(A, Bp, Bp + 4 * 256 - 64, None, 4, 512, TBL, None) == B.RAD_E_ALIAS          # scales in codes

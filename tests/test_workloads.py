@@ -45,3 +45,12 @@ def test_workload_table():
     w = workloads.WORKLOADS
     assert (w["decode_gate_up"].M, w["decode_gate_up"].K, w["decode_gate_up"].N) == (1, 5120, 34816)
     assert w["prefill_down"].G == 68 and w["vocab_head"].G == 40
+
+
+def test_value_ranges_codebook_format():
+    inp = workloads.make(2, 512, 64, workloads.FMT_TBL4_BF16G128, seed=0)
+    assert inp.rscale is None and inp.qw.dtype == np.uint8 and inp.qw.shape == (64, 256)
+    assert inp.gscale.dtype == np.uint16 and inp.gscale.shape == (64, 4)
+    nib = np.concatenate([inp.qw & 15, inp.qw >> 4])
+    assert nib.min() == 0 and nib.max() == 15
+    assert workloads.WORKLOADS["drafter_block"].G == 40

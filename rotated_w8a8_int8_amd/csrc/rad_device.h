@@ -196,26 +196,23 @@ constexpr uint32_t kTbl4_1 = tbl4_dword(-43, -30, -18, -6);
 constexpr uint32_t kTbl4_2 = tbl4_dword(6, 18, 30, 43);
 constexpr uint32_t kTbl4_3 = tbl4_dword(58, 75, 97, 127);
 
-// Four indices (one in the low nibble of each byte of n, high nibbles zero)
-// -> their four int8 table values, in the same byte order.  v_perm picks byte
-// (index mod 8) from the lower or the upper half of the table, bit 3 of the
-// index chooses the half.
-__device__ __forceinline__ uint32_t tbl4_lookup4(uint32_t n) {
-    const uint32_t sel = n & 0x07070707u;
-    const uint32_t lo = __builtin_amdgcn_perm(kTbl4_1, kTbl4_0, sel);   // entries 0..7
-    const uint32_t hi = __builtin_amdgcn_perm(kTbl4_3, kTbl4_2, sel);   // entries 8..15
-    const uint32_t m = ((n >> 3) & 0x01010101u) * 0xFFu;
-    return (hi & m) | (lo & ~m);
-}
 // One 16-byte run of packed indices (32 elements: byte b holds element b in
 // its low nibble and element 16 + b in its high nibble) -> the int8 values of
-// elements 0..15 (lo) and 16..31 (hi).
+// elements 0..15 (lo) and 16..31 (hi).  Per dword of indices: v_perm looks up
+// (index mod 8) in the lower and in the upper half of the table, then a third
+// v_perm picks, byte by byte, the upper result where index bit 3 is set
+// (selector byte i + 4 * bit3); all full-rate bit operations, no multiply.
+__device__ __forceinline__ uint32_t tbl4_lookup4(uint32_t sel7, uint32_t pick) {
+    const uint32_t lo = __builtin_amdgcn_perm(kTbl4_1, kTbl4_0, sel7);   // entries 0..7
+    const uint32_t hi = __builtin_amdgcn_perm(kTbl4_3, kTbl4_2, sel7);   // entries 8..15
+    return __builtin_amdgcn_perm(hi, lo, pick);
+}
 __device__ __forceinline__ void tbl4_decode16(v4i packed, v4i &lo, v4i &hi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w = static_cast<uint32_t>(packed[i]);
-        lo[i] = static_cast<int>(tbl4_lookup4(w & 0x0F0F0F0Fu));
-        hi[i] = static_cast<int>(tbl4_lookup4((w >> 4) & 0x0F0F0F0Fu));
+        lo[i] = static_cast<int>(tbl4_lookup4(w & 0x07070707u, ((w >> 1) & 0x04040404u) | 0x03020100u));
+        hi[i] = static_cast<int>(tbl4_lookup4((w >> 4) & 0x07070707u, ((w >> 5) & 0x04040404u) | 0x03020100u));
     }
 }
 

@@ -363,7 +363,7 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 //
 //   * A workgroup is kSkW compute waves plus one producer wave.  Compute wave
 //     w owns 16 weight rows and streams them from HBM straight into the B
-//     operand of v_mfma_i32_16x16x64_i8, keeping kSkD stages (128 bytes of K
+//     operand of v_mfma_i32_16x16x64_i8, keeping SkShape::D stages (128 bytes of K
 //     each) of its rows in flight in registers.
 //   * The producer wave copies the activation codes of all M tokens, one
 //     128-byte stage of K at a time, into a 3-deep LDS ring with direct
@@ -397,7 +397,6 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 // segments.
 constexpr int kSkStageK = 128;                  // K bytes per stage
 constexpr int kSkRing = 3;                      // activation stages in LDS
-constexpr int kSkD = 4;                         // weight stages in flight per wave
 
 __device__ __forceinline__ int sk_swz(int row) { return row & 7; }
 
@@ -406,10 +405,15 @@ __device__ __forceinline__ int sk_swz(int row) { return row & 7; }
 // which leaves room to read a whole k-step of A fragments before its matrix
 // ops (reading them one by one exposes the LDS latency on every MFMA).  Two
 // workgroups share a CU either way.
+// Shapes per token-block count, measured on MI355X (random int8 weights, the
+// 34816 x 5120 trunk and the 152064 x 5120 head): M <= 16 runs best with few
+// compute waves per workgroup (more workgroups in flight), M <= 64 with seven
+// and a deep weight ring, M <= 128 with five and a shallow one.
 template <int MB> struct SkShape {
-    static constexpr int W = MB <= 4 ? 7 : 5;          // compute waves
-    static constexpr int WPE = MB <= 4 ? 4 : 3;        // waves per SIMD
-    static constexpr int THREADS = 64 * (W + 1);       // plus the producer wave
+    static constexpr int W = MB == 1 ? 3 : MB <= 4 ? 7 : 5;     // compute waves
+    static constexpr int WPE = MB == 1 ? 2 : MB <= 4 ? 4 : 3;   // waves per SIMD
+    static constexpr int D = MB == 1 ? 4 : MB <= 4 ? 6 : 2;     // weight stages in flight per wave
+    static constexpr int THREADS = 64 * (W + 1);                // plus the producer wave
 };
 
 template <int FMT, int MB, bool WRITE_P>
@@ -424,6 +428,7 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
     constexpr int SPG = GW / kSkStageK;               // stages per group
     constexpr int NDMA = ABYTES / 1024;               // producer loads per stage
     constexpr int kSkW = SkShape<MB>::W;
+    constexpr int kSkD = SkShape<MB>::D;
     static_assert(kSkD % SPG == 0, "a ring turn holds whole groups");
     __shared__ __attribute__((aligned(1024))) int8_t As[kSkRing][ABYTES];
 

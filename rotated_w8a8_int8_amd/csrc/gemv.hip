@@ -411,7 +411,7 @@ __device__ __forceinline__ int sk_swz(int row) { return row & 7; }
 // and a deep weight ring, M <= 128 with five and a shallow one.
 template <int MB> struct SkShape {
     static constexpr int W = MB == 1 ? 3 : MB <= 4 ? 7 : 5;     // compute waves
-    static constexpr int WPE = MB == 1 ? 2 : MB <= 4 ? 4 : 3;   // waves per SIMD
+    static constexpr int WPE = MB == 1 ? 2 : 4;                 // waves per SIMD
     static constexpr int D = MB == 1 ? 4 : MB <= 4 ? 6 : 2;     // weight stages in flight per wave
     static constexpr int THREADS = 64 * (W + 1);                // plus the producer wave
 };

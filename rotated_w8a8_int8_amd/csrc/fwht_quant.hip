@@ -82,13 +82,22 @@ __global__ __launch_bounds__(WAVES * 64) void quant_act_kernel(const float *__re
     const float s = a / 127.0f;
     if (threadIdx.x == 0) scale[m] = s;
 
+    // codes through the reciprocal (each element provably equal to the
+    // division's, rare near-half elements redone with it); scales too small
+    // for a finite reciprocal use the division throughout (s is per token,
+    // so the branch is uniform)
+    const bool fast = s >= 0x1p-120f;
+    const float rs = 1.0f / s;
     int8_t *qr = q + m * K;
 #pragma unroll
     for (int it = 0; it < NITER; ++it) {
         const int blk = (it * WAVES + wid) * 4 + (lane >> 4);
         if (blk < nblk) {
             uint32_t lo = 0, hi = 0;
-            if (s != 0.0f) {
+            if (fast) {
+                lo = pack4_rcp(v[it].lo, s, rs);
+                hi = pack4_rcp(v[it].hi, s, rs);
+            } else if (s != 0.0f) {
                 lo = pack4(v[it].lo, s);
                 hi = pack4(v[it].hi, s);
             }

@@ -83,6 +83,36 @@ __device__ __forceinline__ uint32_t pack4(float4 v, float s) {
     return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
+// The same codes through the reciprocal: t = v * fl(1/s) lies within
+// 1.5 * 2^-23 |v / s| (< 2^-15 here, |v / s| <= 127.06) of the rounded
+// quotient fl(v / s), so both round to the same integer unless t is within
+// 2^-13 of a half-integer (about 1 element in 4000).  pack4_rcp codes four
+// elements that way and, if any lane of the wave holds such an element among
+// its four, redoes the four with the IEEE division in a wave-uniform branch
+// (taken for about 6% of the four-element groups of a wave).  Needs s in
+// [2^-120, 2^120] (1/s finite and normal).
+__device__ __forceinline__ float quant1_rcp(float v, float rs, bool &near) {
+    const float t = v * rs;
+    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
+    return __builtin_rintf(t);
+}
+
+__device__ __forceinline__ uint32_t pack4_rcp(float4 v, float s, float rs) {
+    bool near = false;
+    float r0 = quant1_rcp(v.x, rs, near), r1 = quant1_rcp(v.y, rs, near);
+    float r2 = quant1_rcp(v.z, rs, near), r3 = quant1_rcp(v.w, rs, near);
+    if (__any(near)) {
+        r0 = __builtin_rintf(v.x / s);
+        r1 = __builtin_rintf(v.y / s);
+        r2 = __builtin_rintf(v.z / s);
+        r3 = __builtin_rintf(v.w / s);
+    }
+    auto byte = [](float r) {
+        return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f))) & 0xFFu;
+    };
+    return byte(r0) | (byte(r1) << 8) | (byte(r2) << 16) | (byte(r3) << 24);
+}
+
 __device__ __forceinline__ float amax4(float4 v) {
     return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }

@@ -18,9 +18,9 @@
 // 2/4/8 x 1024/2048/4096).  The row amax is a DPP (and for D = 256 a cross-row
 // permute) max inside the row's lanes.  Codes go through x * fl(1/s), which
 // provably rounds like the IEEE quotient unless the product lies within 2^-13
-// of a half-integer; a wave with any such lane redoes its codes with the
-// division (|x / s| <= 127.06 here, so the product and the quotient differ
-// by less than 2^-15).
+// of a half-integer; a wave with any such lane in a group of four values
+// redoes that group with the division (|x / s| <= 127.06 here, so the
+// product and the quotient differ by less than 2^-15).
 #include "rad_device.h"
 #include "rad_launch.h"
 
@@ -104,13 +104,17 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restric
             const uint32_t sb = f16_sat_bits(a / 127.0f);
             const float s = f16_value(sb);
             float q[8];
-            bool near = !(s >= 0x1p-120f);          // s = 0 (f16 scales are never above 65504)
+            const bool tiny = !(s >= 0x1p-120f);    // s = 0 (f16 scales are never above 65504)
             const float rs = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = code_rcp(f[i], rs, near);
-            if (__any(near)) {
+            for (int h = 0; h < 2; ++h) {           // two groups of four, one vote each
+                bool near = tiny;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = code_div(f[i], s);
+                for (int i = 4 * h; i < 4 * h + 4; ++i) q[i] = code_rcp(f[i], rs, near);
+                if (__any(near)) {
+#pragma unroll
+                    for (int i = 4 * h; i < 4 * h + 4; ++i) q[i] = code_div(f[i], s);
+                }
             }
             if (row < rows) {
                 *reinterpret_cast<uint2 *>(codes + row * D + 8 * cl) =

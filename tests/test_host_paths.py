@@ -1,0 +1,58 @@
+"""Host-side behaviour that needs no GPU: the product path refuses to run
+without its HIP library or on CPU tensors (it has no fallback), the
+benchmark refuses more than one GPU, and the product package never imports
+the oracle.
+"""
+import ast
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "rotated_w8a8_int8_amd")
+
+
+def test_binding_raises_when_the_library_is_missing(monkeypatch):
+    from rotated_w8a8_int8_amd import binding as B
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "librad.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    from rotated_w8a8_int8_amd import binding as B
+    x = torch.zeros(2, 128)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.fwht128(x)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        B.quant_act_i8(x)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_product_package_never_imports_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if not f.endswith(".py"):
+                continue
+            tree = ast.parse(open(os.path.join(dirpath, f)).read())
+            for node in ast.walk(tree):
+                names = []
+                if isinstance(node, ast.Import):
+                    names = [a.name for a in node.names]
+                elif isinstance(node, ast.ImportFrom):
+                    names = [node.module or ""]
+                assert not any(n == "oracle" or n.startswith("oracle.") for n in names), (f, names)
+    for dirpath, _, files in os.walk(os.path.join(PKG, "csrc")):
+        for f in files:
+            for line in open(os.path.join(dirpath, f)):
+                if line.lstrip().startswith("#include"):
+                    assert "oracle" not in line, (f, line)

@@ -256,7 +256,7 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
-    ncopies = min(64, max(1, -(-COPY_TARGET_BYTES // sz["weight"]))) if not big else 1
+    ncopies = min(64, max(1, -(-COPY_TARGET_BYTES // sz["weight"])))
     w0 = B.W8A8Weight(to_dev(inp.qw), to_dev(inp.gscale),
                       None if inp.rscale is None else to_dev(inp.rscale), inp.fmt)
     weights = [w0] + [B.W8A8Weight(w0.codes.clone(), w0.gscale.clone(),

@@ -20,10 +20,6 @@ typedef __attribute__((address_space(3))) void lptr_t;
 __device__ __forceinline__ void g2lds_dword(const void *src, void *lds_base) {
     __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_base, 4, 0, 0);
 }
-// The same with 16 bytes per lane: lane l's 16 bytes land at lds_base + 16 l.
-__device__ __forceinline__ void g2lds_16(const void *src, void *lds_base) {
-    __builtin_amdgcn_global_load_lds((gptr_t *)src, (lptr_t *)lds_base, 16, 0, 0);
-}
 
 // bf16 bit pattern -> f32 (a bf16 is the high half of an f32; exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -85,13 +81,6 @@ __device__ __forceinline__ int row4_sum(int v) {
     return v;
 }
 
-// Wave-uniform sum of an int over all 64 lanes (result in a scalar register).
-__device__ __forceinline__ int wave_sum_i32(int v) {
-    v = row16_sum(v);
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // Wave-uniform f32 sum (order fixed: 16-lane butterflies, then rows 0+1+2+3).
 __device__ __forceinline__ float wave_sum_f32(float v) {
     v += lane_xor<1>(v);
@@ -126,39 +115,11 @@ __device__ __forceinline__ int dot16_i8(v4i a, v4i b, int acc) {
     return acc;
 }
 
-// Four 16-byte LDS reads issued together and completed before the block
-// ends (the wait is inside the same asm block, so no output register is ever
-// live while its load is still in flight).  Used where LDS is filled by
-// direct global -> LDS loads: the compiler cannot tell such a read from one
-// that aliases a pending direct load and would otherwise drain every
-// outstanding global load before it; the caller's own vmcnt wait and barrier
-// order these reads instead.  Addresses are LDS byte offsets.
-__device__ __forceinline__ void lds_read4_b128(v4i &r0, v4i &r1, v4i &r2, v4i &r3, uint32_t a0,
-                                               uint32_t a1, uint32_t a2, uint32_t a3) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-        : "memory");
-}
-__device__ __forceinline__ void lds_read2_b128(v4i &r0, v4i &r1, uint32_t a0, uint32_t a1) {
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1)
-        : "v"(a0), "v"(a1)
-        : "memory");
-}
 // Direct global -> LDS loads issued from inline asm.  Same data movement as
-// g2lds_16 / g2lds_dword, but invisible to the compiler's wait-count pass:
-// it therefore neither drains these loads before every later LDS read (as it
-// must for the builtin, not knowing which LDS bytes the load writes) nor
-// tracks them at all.  Callers order them with explicit vmcnt waits and
+// g2lds_dword (and its 16-byte form), but invisible to the compiler's
+// wait-count pass: it therefore neither drains these loads before every later
+// LDS read (as it must for the builtin, not knowing which LDS bytes the load
+// writes) nor tracks them at all.  Callers order them with explicit vmcnt waits and
 // barriers.  Source = sbase (wave-uniform) + voff (per lane, unsigned 32-bit);
 // destination = LDS byte address lds (wave-uniform, passed in M0) + size *
 // lane.  The compiler's hazard checks do not look inside asm, so the block

@@ -20,6 +20,7 @@
 //                    producer wave stages the activation codes of all M
 //                    tokens in LDS for the workgroup.
 #include <algorithm>
+#include <atomic>
 
 #include "rad_device.h"
 #include "rad_launch.h"
@@ -361,10 +362,11 @@ hipError_t launch_m1(const float *x, int8_t *q, float *s, const WeightArgs &w, f
 // The weight stream is the cost (M <= 128 int8 MACs per weight byte is far
 // below the matrix units' ridge), so the kernel is built to keep HBM busy:
 //
-//   * A workgroup is kSkW compute waves plus one producer wave.  Compute wave
-//     w owns 16 weight rows and streams them from HBM straight into the B
-//     operand of v_mfma_i32_16x16x64_i8, keeping SkShape::D stages (128 bytes of K
-//     each) of its rows in flight in registers.
+//   * A workgroup is nw compute waves plus one producer wave (nw chosen at
+//     launch, see sk_compute_waves).  Compute wave w owns 16 weight rows and
+//     streams them from HBM straight into the B operand of
+//     v_mfma_i32_16x16x64_i8, keeping SkShape::D stages (128 bytes of K each)
+//     of its rows in flight in registers.
 //   * The producer wave copies the activation codes of all M tokens, one
 //     128-byte stage of K at a time, into a 3-deep LDS ring with direct
 //     global -> LDS loads, and the compute waves read their A operands from
@@ -400,25 +402,17 @@ constexpr int kSkRing = 3;                      // activation stages in LDS
 
 __device__ __forceinline__ int sk_swz(int row) { return row & 7; }
 
-// Workgroup shape per token block count: up to 64 tokens, 7 compute waves at
-// 4 waves per SIMD (<= 128 registers); above, 5 compute waves at 3 per SIMD,
-// which leaves room to read a whole k-step of A fragments before its matrix
-// ops (reading them one by one exposes the LDS latency on every MFMA).  Two
-// workgroups share a CU either way.
-// Shapes per token-block count, measured on MI355X (random int8 weights, the
-// 34816 x 5120 trunk and the 152064 x 5120 head): M <= 16 runs best with few
-// compute waves per workgroup (more workgroups in flight), M <= 64 with seven
-// and a deep weight ring, M <= 128 with five and a shallow one.
+// Weight stages in flight per compute wave, per token-block count (measured
+// on MI355X, random int8 weights, the 34816 x 5120 trunk and the 152064 x 5120
+// head): deep for up to 64 tokens, shallow above, where the accumulators and
+// a whole k-step of A fragments take the registers.
 template <int MB> struct SkShape {
-    static constexpr int W = MB == 1 ? 3 : MB <= 4 ? 7 : 5;     // compute waves
-    static constexpr int WPE = MB == 1 ? 2 : 4;                 // waves per SIMD
-    static constexpr int D = MB == 1 ? 4 : MB <= 4 ? 6 : 2;     // weight stages in flight per wave
-    static constexpr int THREADS = 64 * (W + 1);                // plus the producer wave
+    static constexpr int D = MB == 1 ? 4 : MB <= 4 ? 6 : 2;
 };
+constexpr int kSkMaxW = 15;                     // compute waves in the largest workgroup
 
 template <int FMT, int MB, bool WRITE_P>
-__global__ __launch_bounds__(SkShape<MB>::THREADS) __attribute__((amdgpu_waves_per_eu(SkShape<MB>::WPE)))
-void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale,
+__global__ __launch_bounds__(64 * (kSkMaxW + 1)) void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale,
                    const int8_t *__restrict__ codes, const void *__restrict__ gscale,
                    const uint16_t *__restrict__ rscale, float *__restrict__ y,
                    int32_t *__restrict__ partials, int M, int N, int K) {
@@ -427,13 +421,13 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
     constexpr int GW = (FMT == kFmtU8) ? 256 : 128;   // K bytes per group
     constexpr int SPG = GW / kSkStageK;               // stages per group
     constexpr int NDMA = ABYTES / 1024;               // producer loads per stage
-    constexpr int kSkW = SkShape<MB>::W;
     constexpr int kSkD = SkShape<MB>::D;
     static_assert(kSkD % SPG == 0, "a ring turn holds whole groups");
     __shared__ __attribute__((aligned(1024))) int8_t As[kSkRing][ABYTES];
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
+    const int nw = static_cast<int>(blockDim.x >> 6) - 1;   // compute waves; the last wave produces
     const int NS = K / kSkStageK;
     const int G = K / GW;
     // Workgroups start their K walk at different groups (and wrap around),
@@ -442,7 +436,7 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
     const int soff = SPG * (static_cast<int>(blockIdx.x) % G);
     auto phys = [&](int s) { return (min(s, NS - 1) + soff) % NS; };   // past the end: re-read
 
-    if (wid == kSkW) {
+    if (wid == nw) {
         // ---- producer.  Load i of a stage fills token rows 8 i .. 8 i + 7:
         // lane l takes row 8 i + l / 8, slot l % 8, i.e. logical chunk
         // (l % 8) ^ swz(row).  Token rows past M repeat row M - 1.
@@ -477,7 +471,7 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
 
     // ---- compute waves
     const int j = lane & 15, qd = lane >> 4;
-    const int n0 = (blockIdx.x * kSkW + wid) * 16;
+    const int n0 = (blockIdx.x * nw + wid) * 16;
     const int nrow = n0 + j;
     const bool nvalid = nrow < N;
     const int nr = min(nrow, N - 1);
@@ -603,13 +597,59 @@ void skinny_kernel(const int8_t *__restrict__ q, const float *__restrict__ scale
         }
 }
 
+// Compute units of the current device, looked up once per device.
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Compute waves per workgroup.  A workgroup costs its rows plus a fixed part
+// that does not shrink with them (its own pass of the M x K activation codes
+// through LDS, the pipeline fill and drain), and a CU runs one wide
+// workgroup at a time, so the kernel takes (rounds of workgroups per CU) x
+// (16 nw + fixed).  Measured on MI355X (256 CUs, M = 16 ... 128, the 34816-,
+// 152064- and 5120-row layers): if one round covers the rows, the narrowest
+// workgroup that does so is fastest (nw = 9 for 34816 rows, 2 for 5120);
+// otherwise the width from 8 to 15 minimising rounds x (16 nw + fixed), with
+// the fixed part worth about 300 rows (nw = 13 for 152064 rows).
+constexpr int kSkFixedRows = 300;
+
+int sk_compute_waves(int64_t N, int cus) {
+    const int64_t tiles = (N + 15) / 16;
+    if (tiles <= static_cast<int64_t>(kSkMaxW) * cus)
+        return static_cast<int>(std::max<int64_t>(1, (tiles + cus - 1) / cus));
+    int best = kSkMaxW;
+    int64_t best_cost = INT64_MAX;
+    for (int w = 8; w <= kSkMaxW; ++w) {
+        const int64_t per_round = static_cast<int64_t>(w) * cus;
+        const int64_t cost = (tiles + per_round - 1) / per_round * (16 * w + kSkFixedRows);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = w;
+        }
+    }
+    return best;
+}
+
 template <int FMT, int MB>
 hipError_t launch_skinny_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                            int32_t *P, hipStream_t st) {
-    const int64_t rows_per_wg = 16 * SkShape<MB>::W;
+    const int cus = device_cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int nw = sk_compute_waves(w.N, cus);
+    const int64_t rows_per_wg = 16 * static_cast<int64_t>(nw);
     const int grid = static_cast<int>((w.N + rows_per_wg - 1) / rows_per_wg);
     auto kern = P ? skinny_kernel<FMT, MB, true> : skinny_kernel<FMT, MB, false>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(SkShape<MB>::THREADS), 0, st, q, s, w.codes, w.gscale, w.rscale, y,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * (nw + 1)), 0, st, q, s, w.codes, w.gscale, w.rscale, y,
                        P, static_cast<int>(M), static_cast<int>(w.N), static_cast<int>(w.K));
     return hipGetLastError();
 }

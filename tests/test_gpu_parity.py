@@ -143,6 +143,22 @@ def test_gemv_small_shapes(torch, M, K, N, fmt):
     assert np.array_equal(host(y2), y)
 
 
+# The M <= 128 kernel picks its workgroup width from N and the CU count: one
+# round of workgroups up to 15 x 16 x CUs rows (12345 rows: four compute waves
+# a workgroup, the last workgroup partly past N), several rounds above (62000
+# and 70001 rows on a 256-CU part).
+@pytest.mark.parametrize("M,K,N,fmt", [(20, 256, 12345, 0), (97, 384, 12345, 1), (3, 256, 70001, 0),
+                                       (40, 256, 62000, 1), (128, 256, 70001, 0)])
+def test_gemv_workgroup_widths(torch, M, K, N, fmt):
+    inp = W.make(M, K, N, fmt, seed=7 * M + N)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+    Pr = oracle.group_partials(q, inp.qw, fmt)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, fmt, inp.gscale, inp.rscale))
+    y2, _ = B.w8a8_gemv(qd, sd, w)
+    assert np.array_equal(host(y2), y)
+
+
 @pytest.mark.parametrize("M", list(range(1, 18)) + [31, 32, 33, 47, 63, 64, 65, 80, 96, 100, 127, 128])
 def test_gemv_m_sweep(torch, M):
     inp = W.make(M, 512, 96, 0, seed=1000 + M)

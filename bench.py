@@ -80,6 +80,11 @@ def parse():
                          "32 candidate rows per token of the workload's weight")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time the vendor int8 GEMM (hipBLASLt through torch._int_mm) on "
+                         "the same activation and weight codes, as context (M > 16, int8 "
+                         "formats): int32 products over all of K, without the group and row "
+                         "scales or the f32 output")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=None,
                     help="run a plain f32 negate kernel that reads BYTES and writes BYTES "
@@ -346,6 +351,34 @@ def main():
     roof["us_per_launch"] = round(ms_k * 1e3, 3)
     roof["traffic"] = load_traffic(wl)
 
+    # ---- context: the vendor's int8 GEMM on the same codes (same stream,
+    # same weight copies, same launch mode).  It computes less than the
+    # contraction above: one int32 sum over all of K per output, no group
+    # scales, no row scale, no f32 epilogue.
+    vendor = None
+    if args.vendor:
+        if wl.M <= 16 or wl.fmt == 2:
+            vendor = {"skipped": "needs M > 16 and int8 codes"}
+        else:
+            outs = [torch.empty((wl.M, wl.N), dtype=torch.int32, device=dev) for _ in range(ncopies)]
+
+            def vendor_call(i):
+                torch._int_mm(q, weights[i].codes.t(), out=outs[i])
+
+            ms_v, _, _ = timed(vendor_call, steps, warmup)
+            vendor = {"library": "hipBLASLt via torch._int_mm",
+                      "computes": "int32 codes x codes^T over all of K; no group or row scales, "
+                                  "int32 output",
+                      "us_per_launch": round(ms_v * 1e3, 3),
+                      "tops": round(sz["ops"] / (ms_v * 1e-3) / 1e12, 2),
+                      "rad_over_vendor_time": round(ms_k / ms_v, 4)}
+            # cross-check on four tokens: the library's exact group partials,
+            # summed over the groups, are the vendor's int32 products
+            _, P4 = B.w8a8_gemv(q[:4], s[:4], weights[0], partials=True)
+            vendor["group_sums_equal_vendor"] = bool(torch.equal(
+                P4.to(torch.int64).sum(dim=2), outs[0][:4].to(torch.int64)))
+            del outs, P4
+
     # ---- parity of the timed buffers against the oracle (sampled rows)
     import oracle
     rows = np.arange(wl.M) if wl.M <= 4 else np.unique(np.linspace(0, wl.M - 1, 4).astype(int))
@@ -402,6 +435,8 @@ def main():
         "cpu_baseline": cpu,
         "parity_on_timed_buffers": parity,
     }
+    if vendor is not None:
+        out["vendor_int8_gemm"] = vendor
     print(json.dumps(out))
 
 

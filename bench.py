@@ -5,6 +5,7 @@
     python bench.py --op quant_weight [--workload NAME]
     python bench.py --op kv_quant | kv_dequant [--workload kv_200k]
     python bench.py --op rescore [--workload vocab_head]
+    python bench.py --op fwht | quant_act [--workload prefill_down]
 
 A step is one pass of the whole layer over one batch of synthetic input that
 is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
@@ -39,6 +40,13 @@ encode reads bf16 and writes codes and f16 scales, decode the reverse; both
 are HBM streams, so `roofline` is their algorithmic bytes per second against
 the 8 TB/s HBM peak.
 
+--op fwht / quant_act time the activation side alone on the workload's f32
+activations (default prefill_down, 8192 x 17408): rad_fwht128 reads and writes
+f32 (8 bytes per element), rad_quant_act_i8 with rotation reads f32 and writes
+int8 codes plus one f32 scale per token (5 bytes per element + 4 per token);
+both are HBM streams against the 8 TB/s peak, launched eagerly over enough
+copies of the activations to exceed the last-level cache.
+
 --op rescore times rad_w8a8_rescore on the workload's weight (default the
 vocabulary head) with 32 distinct candidate rows per token: 64 different
 candidate sets are cycled through a HIP graph so the gathered rows come from
@@ -72,7 +80,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode_gate_up")
-    ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore"),
+    ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore",
+                                     "fwht", "quant_act"),
                     default="linear",
                     help="linear: the whole layer (default); quant_weight: the weight-side "
                          "quantiser on the workload's weight shape; kv_quant / kv_dequant: "
@@ -243,6 +252,9 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.op == "quant_weight":
         bench_quant_weight(args, wl)
+        return
+    if args.op in ("fwht", "quant_act"):
+        bench_act(args, W.WORKLOADS["prefill_down"] if args.workload == "decode_gate_up" else wl)
         return
     if args.op == "rescore":
         bench_rescore(args, W.WORKLOADS["vocab_head"] if args.workload == "decode_gate_up" else wl)
@@ -618,6 +630,104 @@ def bench_rescore(args, wl):
         "data": "synthetic",
         "config": {"workload": "rescore_" + wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "candidates": C,
                    "candidate_sets": nsets, "launch": "hip_graph"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_on_timed_buffers": parity,
+    }))
+
+
+def bench_act(args, wl):
+    """rad_fwht128 or rad_quant_act_i8 (rotate on) alone, on the workload's f32 activations."""
+    import torch
+    import oracle
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
+    fwht = args.op == "fwht"
+    M, K = wl.M, wl.K
+    steps = args.steps if args.steps is not None else 100
+    warmup = args.warmup if args.warmup is not None else 10
+    x = W.make_workload(wl.name).x
+    dev = torch.device("cuda", 0)
+    per = M * K * (8 if fwht else 5)
+    ncopies = max(1, min(8, -(-COPY_TARGET_BYTES // per)))
+    xs = [torch.from_numpy(x).to(dev) for _ in range(ncopies)]
+    if fwht:
+        outs = [torch.empty((M, K), dtype=torch.float32, device=dev) for _ in range(ncopies)]
+    else:
+        outs = [(torch.empty((M, K), dtype=torch.int8, device=dev),
+                 torch.empty((M,), dtype=torch.float32, device=dev)) for _ in range(ncopies)]
+
+    def call(i):
+        if fwht:
+            B.fwht128(xs[i], out=outs[i])
+        else:
+            B.quant_act_i8(xs[i], rotate=True, q=outs[i][0], scale=outs[i][1])
+
+    stream = torch.cuda.Stream(device=dev)             # default priority
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            call(i % ncopies)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            call(i % ncopies)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    alg = M * K * 8 if fwht else M * K * 5 + M * 4
+    value = alg / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "rad_fwht128" if fwht else "rad_quant_act_i8",
+            "bytes_per_launch": alg, "us_per_launch": round(ms * 1e3, 3)}
+    rows = np.unique(np.linspace(0, M - 1, 8).astype(int))
+    parity = True
+    if fwht:
+        ref = oracle.fwht128(x[rows])
+        for o in outs:
+            parity = parity and bool(np.array_equal(o.cpu().numpy()[rows].view(np.uint32), ref.view(np.uint32)))
+    else:
+        qo, so = oracle.quant_act_i8(x[rows])
+        for q, sc in outs:
+            parity = parity and bool(np.array_equal(q.cpu().numpy()[rows], qo))
+            parity = parity and bool(np.array_equal(sc.cpu().numpy()[rows].view(np.uint32), so.view(np.uint32)))
+    cpu = None
+    if not args.no_cpu_baseline:
+        nrow = min(M, 64)
+        xs_h = np.ascontiguousarray(x[:nrow])
+        n = 0
+        c0 = time.perf_counter()
+        while True:
+            if fwht:
+                oracle.fwht128(xs_h)
+            else:
+                oracle.quant_act_i8(xs_h)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        dt = (time.perf_counter() - c0) / n
+        cpu = {"value": round(alg * nrow / M / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": "%d of %d tokens, %d repetitions, %.1f s" % (nrow, M, n, dt * n)}
+    print(json.dumps({
+        "metric": ("fwht128 rotation: HBM GB/s (f32 in, f32 out)" if fwht else
+                   "rotate + per-token int8 quantise: HBM GB/s (f32 in, int8 codes + f32 scale out)"),
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s_%s" % (args.op, wl.name), "M": M, "K": K, "copies": ncopies,
+                   "launch": "eager"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_on_timed_buffers": parity,

@@ -38,6 +38,18 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2 and "one GPU" in r.stderr
 
 
+@pytest.mark.parametrize("args", [["--op", "fwht"], ["--op", "quant_act"],
+                                  ["--workload", "prefill_down", "--vendor"]])
+def test_bench_options_parse_and_need_a_gpu(args):
+    # every bench leg is GPU work: without a GPU it stops before timing anything
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1 and "needs a GPU" in r.stderr, r.stderr
+
+
 def test_product_package_never_imports_the_oracle():
     for dirpath, _, files in os.walk(PKG):
         for f in files:

@@ -16,7 +16,9 @@ decode of the fused gate_up projection (M=1, K=5120, N=34816).
 
 The weights rotate over enough distinct copies (>= 1 GiB) that the 256 MiB
 last-level cache cannot serve a repeated read.  Steps are replayed from a HIP
-graph (one graph launch per round of copies) unless --eager is given.
+graph unless --eager is given: one graph holds one round of the copies for
+M > 128, and about 64 steps (several rounds) for M <= 128, as an engine
+captures a whole forward pass.
 
 One JSON line is printed.  `value` is the step's algorithmic bytes (f32
 activations in, weight codes and scales in, f32 outputs out, each counted
@@ -295,12 +297,18 @@ def main():
     stream = torch.cuda.Stream(device=dev)             # default priority
     torch.cuda.synchronize()
 
+    # calls per graph: for the short M <= 128 steps, several rounds over the
+    # weight copies go into one graph (as an engine captures a whole forward
+    # pass), so the per-replay launch cost is not charged to a handful of steps
+    per_round = ncopies * (1 if big else max(1, -(-64 // ncopies)))
+
     def make_round(fn):
-        """One round = one call per weight copy; graph-captured unless --eager."""
+        """One round = per_round calls, cycling over the weight copies;
+        graph-captured unless --eager."""
         if args.eager:
             def run():
-                for i in range(ncopies):
-                    fn(i)
+                for i in range(per_round):
+                    fn(i % ncopies)
             return run
         with torch.cuda.stream(stream):
             for i in range(ncopies):                   # warm the code path before capture
@@ -308,15 +316,15 @@ def main():
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for i in range(ncopies):
-                fn(i)
+            for i in range(per_round):
+                fn(i % ncopies)
         torch.cuda.synchronize()
         return g.replay
 
     def timed(fn, n_calls, n_warm):
         run = make_round(fn)
-        rounds = max(1, -(-n_calls // ncopies))
-        wrounds = max(1, -(-n_warm // ncopies)) if n_warm > 0 else 0
+        rounds = max(1, -(-n_calls // per_round))
+        wrounds = max(1, -(-n_warm // per_round)) if n_warm > 0 else 0
         with torch.cuda.stream(stream):
             for _ in range(wrounds):
                 run()
@@ -331,7 +339,7 @@ def main():
             torch.cuda.synchronize()
             t1 = time.perf_counter()
         ms = e0.elapsed_time(e1)
-        return ms / (rounds * ncopies), (t1 - t0) * 1e3 / (rounds * ncopies), rounds * ncopies
+        return ms / (rounds * per_round), (t1 - t0) * 1e3 / (rounds * per_round), rounds * per_round
 
     # ---- the whole step
     ms_step, wall_ms_step, nsteps = timed(step, steps, warmup)
@@ -442,6 +450,7 @@ def main():
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
                    "format": {0: "u8g256_bf16row", 1: "bf16g128", 2: "tbl4_bf16g128"}[wl.fmt],
                    "weight_copies": ncopies, "launch": "eager" if args.eager else "hip_graph",
+                   "steps_per_launch": 1 if args.eager else per_round,
                    "host_ms_per_step": round(wall_ms_step, 5)},
         "roofline": roof,
         "cpu_baseline": cpu,

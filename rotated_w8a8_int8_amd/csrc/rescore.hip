@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void rescore_kernel(const int8_t *__restrict__
         for (int u = 0; u < kRsPass; ++u) {
             const int c = c0 + 64 * u + lane;
             if (c < nchunk) {
-                w[u] = ld16(wrow + 16 * c);
+                w[u] = ld16_nt(wrow + 16 * c);
                 a[u] = ld16(qrow + 16 * c);
             }
         }

@@ -184,12 +184,5 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
 
 // Loads that bypass nothing: plain 16-byte global loads.
 __device__ __forceinline__ v4i ld16(const void *p) { return *reinterpret_cast<const v4i *>(p); }
-// 16-byte nontemporal loads (global_load_dwordx4 ... nt), for data a call
-// reads once in short scattered runs (gathered weight rows).  Measured on the
-// streaming kernels they are slower than plain loads, so only the gather
-// uses them.
-__device__ __forceinline__ v4i ld16_nt(const void *p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
-}
 
 }  // namespace rad

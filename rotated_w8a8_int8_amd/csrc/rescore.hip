@@ -24,6 +24,13 @@
 namespace rad {
 namespace {
 
+// 16-byte nontemporal loads (global_load_dwordx4 ... nt) for the gathered
+// weight rows, which one call reads once in short scattered runs: measured
+// faster here than plain loads (the streaming kernels measured the reverse).
+__device__ __forceinline__ v4i ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const v4i *>(p));
+}
+
 constexpr int kFmtU8 = 0;
 constexpr int kRsPass = 8;     // chunks per lane per pass (K = 8192 in one pass)
 

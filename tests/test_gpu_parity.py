@@ -168,6 +168,24 @@ def test_gemv_m_sweep(torch, M):
     assert_rows_close(y, oracle.epilogue(Pr, s, 0, inp.gscale, inp.rscale))
 
 
+# 33..64 tokens in the int8 formats run the kernel that stages both operands
+# through LDS: ragged weight-row counts (a last workgroup partly past N), a
+# group-scale array of 5 bytes (its last dword is moved back to end at the
+# array's end), one and many stages of K; the head format with an odd number
+# of groups takes the register-streaming kernel instead.
+@pytest.mark.parametrize("M,K,N,fmt", [(33, 256, 5, 0), (48, 256, 129, 0), (64, 2048, 130, 1),
+                                       (40, 5120, 1000, 0), (64, 256, 257, 1), (50, 384, 70, 1),
+                                       (34, 1280, 383, 0), (63, 768, 128, 1)])
+def test_gemv_lds_path_shapes(torch, M, K, N, fmt):
+    inp = W.make(M, K, N, fmt, seed=11 * M + K + N)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+    Pr = oracle.group_partials(q, inp.qw, fmt)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, fmt, inp.gscale, inp.rscale))
+    y2, _ = B.w8a8_gemv(qd, sd, w)
+    assert np.array_equal(host(y2), y)
+
+
 def test_gemv_m1_u8_output_is_exact(torch):
     # the M = 1 path sums u8 * P exactly and applies s * r * 2^-7 in f64 in the
     # oracle's order, so its output equals the oracle's bit for bit

@@ -127,12 +127,30 @@ def sizes(wl):
     )
 
 
+def lds_kernel_applies(wl, cus=256):
+    """Whether the M <= 128 path runs the LDS-staged kernel for this workload on
+    a part with `cus` compute units (the library's own rule: 33..64 or
+    112..128 tokens, int8 formats, workgroups of 128 or 144 weight rows
+    filling at least 85% of their rounds)."""
+    if wl.K % 256 or not (wl.fmt == 0 or (wl.fmt == 1 and (wl.K // 128) % 2 == 0)):
+        return False
+    if 33 <= wl.M <= 64:
+        bn = 128
+    elif 112 <= wl.M <= 128:
+        bn = 144
+    else:
+        return False
+    wgs = -(-wl.N // bn)
+    rounds = -(-wgs // cus)
+    return wgs * 100 >= 85 * rounds * cus
+
+
 def kernel_sources(wl):
     """The source files the dominant kernel of a workload's step is built from."""
     common = ["rad_device.h", "rad_launch.h"]
     if wl.M == 1:
         return ["gemv.hip", "rotate_quant.h"] + common       # the fused one-token kernel
-    if 33 <= wl.M <= 64 and wl.K % 256 == 0 and (wl.fmt == 0 or (wl.fmt == 1 and (wl.K // 128) % 2 == 0)):
+    if lds_kernel_applies(wl):
         return ["skinny_lds.hip"] + common                  # both operands staged through LDS
     if wl.M <= 128:
         return ["gemv.hip"] + common

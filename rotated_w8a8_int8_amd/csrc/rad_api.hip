@@ -72,8 +72,8 @@ rad::WeightArgs weight_args(const rad_w8a8_weight *w) {
 
 }  // namespace
 
-// 2..128 tokens: the LDS-staged kernel where it applies (33..64 tokens,
-// int8 formats), else the register-streaming one.
+// 2..128 tokens: the LDS-staged kernel where it applies, else the
+// register-streaming one.
 static hipError_t launch_small(const int8_t *q, const float *s, const rad::WeightArgs &w, float *y,
                                int64_t M, int32_t *P, hipStream_t st) {
     if (rad::skinny_lds_supported(w, M)) return rad::launch_skinny_lds(q, s, w, y, M, P, st);

@@ -1,5 +1,6 @@
-// skinny_lds.hip -- rotated W8A8 contraction + epilogue for 33..64 tokens
-// with both operands staged through LDS (gfx950).
+// skinny_lds.hip -- rotated W8A8 contraction + epilogue for 33..64 and
+// 112..128 tokens with both operands staged through LDS (gfx950), where the
+// workgroups fill their rounds (skinny_lds_supported).
 //
 // What is computed (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance
 // container", table rows "Weights" and "Activations"): exact int32 partials
@@ -7,8 +8,8 @@
 // scale and a bf16 row scale, or 128 with a bf16 scale for the head), folded
 // per group into f32, then y = s_m * (r_n) * 2^-7 * sum_g scale[n][g] * P.
 //
-// A 512-thread workgroup owns 128 weight rows and all (up to 64) tokens.  K
-// is walked in 256-byte stages through a 3-deep LDS ring filled by direct
+// A workgroup owns 16 weight rows per wave and all tokens (see SlShape).  K
+// is walked in 256-byte stages through an LDS ring filled by direct
 // global -> LDS 16-byte loads: one load instruction covers four rows x 256
 // contiguous bytes (the weight stream is the cost, and it streams fastest in
 // long runs per row), activation rows likewise.  Wave w computes its 16
@@ -23,6 +24,8 @@
 // LDS: row r of a stage occupies 256 bytes; its logical 16-byte chunk c sits
 // in slot c ^ (r & 7), so the eight rows an operand read covers at a time hit
 // eight different 16-byte slots of a 128-byte bank line.
+#include <atomic>
+
 #include "rad_device.h"
 #include "rad_launch.h"
 
@@ -30,55 +33,64 @@ namespace rad {
 namespace {
 
 constexpr int kFmtU8 = 0;
-constexpr int kSlWaves = 8;                        // 8 waves x 16 weight rows
-constexpr int kSlBN = 16 * kSlWaves;               // weight rows per workgroup
-constexpr int kSlMP = 64;                          // token rows (padded)
 constexpr int kSlKC = 256;                         // K bytes per stage
-constexpr int kSlStages = 3;
-constexpr int kSlA = kSlMP * kSlKC;                // 16 KiB
-constexpr int kSlB = kSlBN * kSlKC;                // 32 KiB
-constexpr int kSlDmaA = kSlA / 1024 / kSlWaves;    // 1 KiB loads per wave per stage
-constexpr int kSlDmaB = kSlB / 1024 / kSlWaves;
-constexpr int kSlDma = kSlDmaA + kSlDmaB + 1;      // + the scale dword load
-static_assert(kSlDmaA * kSlWaves * 1024 == kSlA && kSlDmaB * kSlWaves * 1024 == kSlB, "stage split");
+
+// A workgroup shape: MB blocks of 16 tokens, NW waves of 16 weight rows, NST
+// stages in the LDS ring.  Each wave issues the same number of 1 KiB direct
+// loads per stage (the explicit waits count them); where a stage's blocks do
+// not split evenly over the waves, the remainder loads a valid block again
+// into a spare LDS area nobody reads.
+template <int MB_, int NW_, int NST_> struct SlShape {
+    static constexpr int MB = MB_, NW = NW_, NST = NST_;
+    static constexpr int MP = 16 * MB, BN = 16 * NW;
+    static constexpr int A = MP * kSlKC, B = BN * kSlKC;           // bytes per stage
+    static constexpr int NA = A / 1024, NB = B / 1024;             // 1 KiB blocks per stage
+    static constexpr int DA = (NA + NW - 1) / NW, DB = (NB + NW - 1) / NW;
+    static constexpr int SPARE = DA * NW - NA + DB * NW - NB;      // spare blocks
+    static constexpr int DMA = DA + DB + 1;                        // + the scale dword load
+};
 
 __device__ __forceinline__ int sl_addr(int row, int c) { return 256 * row + 16 * (c ^ (row & 7)); }
 
-template <int FMT, bool WRITE_P>
-__global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
+template <int FMT, class S, bool WRITE_P>
+__global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ scale, const int8_t *__restrict__ codes,
     const void *__restrict__ gscale, const uint16_t *__restrict__ rscale, float *__restrict__ y,
     int32_t *__restrict__ partials, int M, int N, int K) {
+    constexpr int MB = S::MB, NST = S::NST, DA = S::DA, DB = S::DB;
     constexpr int GPS = (FMT == kFmtU8) ? 1 : 2;      // groups per stage
     constexpr int KPG = 4 / GPS;                       // k-steps per group
     constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;       // bytes per group scale
-    __shared__ __attribute__((aligned(1024))) int8_t As[kSlStages][kSlA];
-    __shared__ __attribute__((aligned(1024))) int8_t Bs[kSlStages][kSlB];
-    __shared__ __attribute__((aligned(256))) uint32_t Ss[kSlStages][kSlWaves][64];
+    __shared__ __attribute__((aligned(1024))) int8_t As[NST][S::A];
+    __shared__ __attribute__((aligned(1024))) int8_t Bs[NST][S::B];
+    __shared__ __attribute__((aligned(1024))) int8_t Xs[S::SPARE > 0 ? S::SPARE * 1024 : 16];
+    __shared__ __attribute__((aligned(256))) uint32_t Ss[NST][S::NW][64];
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
     const int wu = __builtin_amdgcn_readfirstlane(wid);
     const int j = lane & 15, qd = lane >> 4;
-    const int n0 = static_cast<int>(blockIdx.x) * kSlBN;
+    const int n0 = static_cast<int>(blockIdx.x) * S::BN;
     const int NS = K / kSlKC;
     const int G = K / (kSlKC / GPS);
 
-    // ---- direct loads of one stage.  Load i of wave w fills 1 KiB block b:
-    // four rows 4 b .. 4 b + 3 (lane l: row 4 b + l / 16, slot l % 16, i.e.
-    // logical chunk (l % 16) ^ (row & 7)).  Rows past M or N repeat the last
-    // row (never stored).
+    // ---- direct loads of one stage.  Block b of an operand holds its rows
+    // 4 b .. 4 b + 3 (lane l: row 4 b + l / 16, slot l % 16, i.e. logical
+    // chunk (l % 16) ^ (row & 7)).  Rows past M or N repeat the last row
+    // (never stored); block numbers past the operand's re-load block 0.
     const int dr = lane >> 4, dslot = lane & 15;
-    uint32_t aoffs[kSlDmaA], boffs[kSlDmaB];
+    uint32_t aoffs[DA], boffs[DB];
 #pragma unroll
-    for (int i = 0; i < kSlDmaA; ++i) {
-        const int row = 4 * (wid * kSlDmaA + i) + dr;
+    for (int i = 0; i < DA; ++i) {
+        const int blk = wid * DA + i;
+        const int row = blk < S::NA ? 4 * blk + dr : dr;
         aoffs[i] = static_cast<uint32_t>(min(row, M - 1)) * static_cast<uint32_t>(K) +
                    16u * static_cast<uint32_t>(dslot ^ (row & 7));
     }
 #pragma unroll
-    for (int i = 0; i < kSlDmaB; ++i) {
-        const int row = 4 * (wid * kSlDmaB + i) + dr;
+    for (int i = 0; i < DB; ++i) {
+        const int blk = wid * DB + i;
+        const int row = blk < S::NB ? 4 * blk + dr : dr;
         boffs[i] = static_cast<uint32_t>(min(n0 + row, N - 1) - n0) * static_cast<uint32_t>(K) +
                    16u * static_cast<uint32_t>(dslot ^ (row & 7));
     }
@@ -98,22 +110,30 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
     // again, so every wait count below is uniform
     auto issue_stage = [&](int s) {
         const int sc = min(s, NS - 1);
-        const int buf = s % kSlStages;
+        const int buf = s % NST;
+        // block numbers are wave-major, so the padding blocks of each operand
+        // form one range: A's first, then B's, in the spare area
 #pragma unroll
-        for (int i = 0; i < kSlDmaA; ++i)
-            dma16(q + static_cast<int64_t>(sc) * kSlKC, aoffs[i],
-                  lds_offset(&As[buf][(wu * kSlDmaA + i) * 1024]));
+        for (int i = 0; i < DA; ++i) {
+            const int blk = wu * DA + i;
+            const uint32_t dst = blk < S::NA ? lds_offset(&As[buf][0]) + 1024u * blk
+                                             : lds_offset(&Xs[0]) + 1024u * (blk - S::NA);
+            dma16(q + static_cast<int64_t>(sc) * kSlKC, aoffs[i], dst);
+        }
 #pragma unroll
-        for (int i = 0; i < kSlDmaB; ++i)
-            dma16(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i],
-                  lds_offset(&Bs[buf][(wu * kSlDmaB + i) * 1024]));
+        for (int i = 0; i < DB; ++i) {
+            const int blk = wu * DB + i;
+            const uint32_t dst = blk < S::NB ? lds_offset(&Bs[buf][0]) + 1024u * blk
+                                             : lds_offset(&Xs[0]) + 1024u * (DA * S::NW - S::NA + blk - S::NB);
+            dma16(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
+        }
         dma4(gscale, static_cast<uint32_t>(sc_dword(sc)), lds_offset(&Ss[buf][wu][0]));
     };
 
-    v4i P[4];
-    float F[4][4];
+    v4i P[MB];
+    float F[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
         P[mb] = v4i{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) F[mb][e] = 0.0f;
@@ -121,22 +141,23 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
 
     // LDS offsets of this lane's fragments at k-step 0 (row j of each 16-row
     // block, chunk qd); k-step kk reads chunk 4 kk + qd, i.e. offset XOR 64 kk
-    int aoff[4];
+    int aoff[MB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) aoff[mb] = sl_addr(16 * mb + j, qd);
+    for (int mb = 0; mb < MB; ++mb) aoff[mb] = sl_addr(16 * mb + j, qd);
     const int boff = sl_addr(16 * wid + j, qd);
 
-    issue_stage(0);
-    issue_stage(1);
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue_stage(p);
     for (int s = 0; s < NS; ++s) {
-        // stage s has landed once at most the next stage's loads remain
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSlDma) : "memory");
+        // stage s has landed once at most the loads of the NST - 2 stages
+        // issued after it remain
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * S::DMA) : "memory");
         // every wave's loads of stage s are in LDS, and every wave is done
         // with stage s - 1, whose buffer the next issue overwrites
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_stage(s + 2);
-        const int buf = s % kSlStages;
+        issue_stage(s + NST - 1);
+        const int buf = s % NST;
         const int8_t *Ab = As[buf];
         const int8_t *Bb = Bs[buf];
         const uint32_t sw = Ss[buf][wid][j];
@@ -144,11 +165,11 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const v4i b = *reinterpret_cast<const v4i *>(Bb + (boff ^ (64 * kk)));
-            v4i a[4];
+            v4i a[MB];
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + (aoff[mb] ^ (64 * kk)));
+            for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + (aoff[mb] ^ (64 * kk)));
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
                 P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb], b, (kk % KPG == 0) ? v4i{0, 0, 0, 0} : P[mb],
                                                                0, 0, 0);
             if (kk % KPG == KPG - 1) {
@@ -159,7 +180,7 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
                 else
                     sc = bf16_to_f32(static_cast<uint16_t>((sw >> (shift + 16 * gi)) & 0xFFFFu));
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
+                for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) F[mb][e] += static_cast<float>(P[mb][e]) * sc;
                     if constexpr (WRITE_P) {
@@ -182,7 +203,7 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
     float rn = 0x1p-7f;
     if constexpr (FMT == kFmtU8) rn = bf16_to_f32(rscale[nrow]) * 0x1p-7f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = 16 * mb + 4 * qd + e;
@@ -190,30 +211,70 @@ __global__ __launch_bounds__(64 * kSlWaves) void skinny_lds_kernel(
         }
 }
 
-template <int FMT>
+using Shape64 = SlShape<4, 8, 3>;     // 33..64 tokens: 128 rows, 3 stages of 48 KiB
+using Shape128 = SlShape<8, 9, 2>;    // 65..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+
+template <int FMT, class S>
 hipError_t launch_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                     int32_t *P, hipStream_t st) {
-    const int64_t grid = (w.N + kSlBN - 1) / kSlBN;
-    auto kern = P ? skinny_lds_kernel<FMT, true> : skinny_lds_kernel<FMT, false>;
-    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(64 * kSlWaves), 0, st, q, s, w.codes,
+    const int64_t grid = (w.N + S::BN - 1) / S::BN;
+    auto kern = P ? skinny_lds_kernel<FMT, S, true> : skinny_lds_kernel<FMT, S, false>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(64 * S::NW), 0, st, q, s, w.codes,
                        w.gscale, w.rscale, y, P, static_cast<int>(M), static_cast<int>(w.N),
                        static_cast<int>(w.K));
     return hipGetLastError();
 }
 
+// Compute units of the current device, looked up once per device.
+int lds_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
+// A CU holds one of these workgroups at a time (LDS), so the kernel takes
+// whole rounds of workgroups; it is used only where its workgroups fill at
+// least 85% of their rounds.  Measured on MI355X (256 CUs, K = 5120): the
+// 152064-row head at 64 tokens (1188 workgroups, 93%) 189 us against 208 us
+// for the register-streaming kernel; the 34816-row trunk at 33..64 tokens
+// (272 workgroups, 53%) 55-59 us against 40-43 us, so that shape keeps the
+// other kernel; at 112..128 tokens the 144-row workgroups (242, one round)
+// beat it by 1-4%, at 65..96 tokens (padded to 128) they lose.
 bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
-    if (M < 33 || M > kSlMP || w.K % kSlKC != 0) return false;
-    if (w.fmt == kFmtU8) return w.N * (w.K / 256) >= 4;
-    if (w.fmt == 1) return (w.K / 128) % 2 == 0;   // head: the stage's two scales share a dword
-    return false;
+    if (w.K % kSlKC != 0) return false;
+    if (w.fmt == kFmtU8) {
+        if (w.N * (w.K / 256) < 4) return false;
+    } else if (w.fmt != 1 || (w.K / 128) % 2 != 0) {   // head: the stage's two scales share a dword
+        return false;
+    }
+    int64_t bn;
+    if (M >= 33 && M <= 64) bn = Shape64::BN;
+    else if (M >= 112 && M <= 128) bn = Shape128::BN;
+    else return false;
+    const int cus = lds_cu_count();
+    if (cus <= 0) return false;
+    const int64_t wgs = (w.N + bn - 1) / bn;
+    const int64_t rounds = (wgs + cus - 1) / cus;
+    return wgs * 100 >= 85 * rounds * cus;
 }
 
 hipError_t launch_skinny_lds(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                              int32_t *partials, hipStream_t st) {
-    return w.fmt == kFmtU8 ? launch_t<0>(q, s, w, y, M, partials, st)
-                           : launch_t<1>(q, s, w, y, M, partials, st);
+    if (M <= 64)
+        return w.fmt == kFmtU8 ? launch_t<0, Shape64>(q, s, w, y, M, partials, st)
+                               : launch_t<1, Shape64>(q, s, w, y, M, partials, st);
+    return w.fmt == kFmtU8 ? launch_t<0, Shape128>(q, s, w, y, M, partials, st)
+                           : launch_t<1, Shape128>(q, s, w, y, M, partials, st);
 }
 
 }  // namespace rad

@@ -168,14 +168,16 @@ def test_gemv_m_sweep(torch, M):
     assert_rows_close(y, oracle.epilogue(Pr, s, 0, inp.gscale, inp.rscale))
 
 
-# 33..64 tokens in the int8 formats run the kernel that stages both operands
-# through LDS: ragged weight-row counts (a last workgroup partly past N), a
-# group-scale array of 5 bytes (its last dword is moved back to end at the
-# array's end), one and many stages of K; the head format with an odd number
-# of groups takes the register-streaming kernel instead.
-@pytest.mark.parametrize("M,K,N,fmt", [(33, 256, 5, 0), (48, 256, 129, 0), (64, 2048, 130, 1),
-                                       (40, 5120, 1000, 0), (64, 256, 257, 1), (50, 384, 70, 1),
-                                       (34, 1280, 383, 0), (63, 768, 128, 1)])
+# The kernel that stages both operands through LDS runs 33..64 and 112..128
+# tokens in the int8 formats where its workgroups (128 or 144 weight rows)
+# fill at least 85% of their rounds over the CUs; on a 256-CU MI355X these
+# shapes take it: ragged last workgroups, one and two rounds, one and many
+# stages of K, both formats.  Small weights and the head format with an odd
+# number of groups take the register-streaming kernel (last two cases).
+@pytest.mark.parametrize("M,K,N,fmt", [(33, 256, 30000, 0), (48, 512, 30001, 0), (64, 2048, 28000, 1),
+                                       (40, 256, 65466, 0), (64, 768, 30100, 1), (128, 256, 33000, 0),
+                                       (120, 512, 34000, 1), (112, 256, 31400, 0),
+                                       (64, 256, 5, 0), (50, 384, 70, 1)])
 def test_gemv_lds_path_shapes(torch, M, K, N, fmt):
     inp = W.make(M, K, N, fmt, seed=11 * M + K + N)
     q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)

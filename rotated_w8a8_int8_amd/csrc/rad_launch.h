@@ -21,9 +21,9 @@ hipError_t launch_quant_act(const float *x, int8_t *q, float *s, int64_t M, int6
                             hipStream_t st);
 hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st);
-// 33..64 or 112..128 tokens, int8 formats (head: an even number of groups),
-// enough weight rows to fill the rounds of workgroups: both operands staged
-// through LDS.
+// 33..64 or 112..128 tokens in the int8 formats (head: an even number of
+// groups), 9..16 tokens in the codebook format, enough weight rows to fill
+// the rounds of workgroups: both operands staged through LDS.
 bool skinny_lds_supported(const WeightArgs &w, int64_t M);
 hipError_t launch_skinny_lds(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                              int32_t *partials, hipStream_t st);

@@ -1,5 +1,6 @@
-// skinny_lds.hip -- rotated W8A8 contraction + epilogue for 33..64 and
-// 112..128 tokens with both operands staged through LDS (gfx950), where the
+// skinny_lds.hip -- rotated W8A8 contraction + epilogue with both operands
+// staged through LDS (gfx950): 33..64 and 112..128 tokens in the int8
+// formats, 9..16 tokens in the drafter's 4-bit codebook format, where the
 // workgroups fill their rounds (skinny_lds_supported).
 //
 // What is computed (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance
@@ -211,8 +212,167 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
         }
 }
 
+// 4-bit codebook format: a stage is 256 bytes of each weight row's packed
+// indices (512 elements, four 128-element groups with a bf16 scale each) and
+// 512 bytes of each token row.  Weight blocks are four rows x 256 bytes as
+// above; token blocks are two rows x 512 bytes (lane l: row 2 b + l / 32,
+// slot l % 32).  Lane j + 16 q expands run 4 p + q of its weight row (32
+// elements: low nibbles 0..15, high nibbles 16..31) for k-steps 2 p and
+// 2 p + 1, and reads the matching token chunks 8 p + 2 q and 8 p + 2 q + 1, so
+// k-steps 2 p, 2 p + 1 cover exactly group p of the stage.  Each wave fetches
+// its rows' two scale dwords per stage (groups 4 s .. 4 s + 3).
+template <class S, bool WRITE_P>
+__global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ scale, const int8_t *__restrict__ codes,
+    const void *__restrict__ gscale, float *__restrict__ y, int32_t *__restrict__ partials, int M, int N,
+    int K) {
+    constexpr int MB = S::MB, NST = S::NST, NW = S::NW;
+    constexpr int RA = 2 * kSlKC;                      // token-row bytes per stage
+    constexpr int ABYTES = S::MP * RA, BBYTES = S::BN * kSlKC;
+    constexpr int NA = ABYTES / 1024, NB = BBYTES / 1024;
+    constexpr int DA = (NA + NW - 1) / NW, DB = (NB + NW - 1) / NW;
+    constexpr int SPARE = DA * NW - NA + DB * NW - NB;
+    constexpr int DMA = DA + DB + 2;                   // + two scale dwords
+    __shared__ __attribute__((aligned(1024))) int8_t As[NST][ABYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t Bs[NST][BBYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t Xs[SPARE > 0 ? SPARE * 1024 : 16];
+    __shared__ __attribute__((aligned(256))) uint32_t Ss[NST][NW][2][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(wid);
+    const int j = lane & 15, qd = lane >> 4;
+    const int n0 = static_cast<int>(blockIdx.x) * S::BN;
+    const int NS = K / RA;
+    const int G = K / 128;
+    const int RB = K / 2;                              // packed bytes of a weight row
+
+    uint32_t aoffs[DA], boffs[DB];
+#pragma unroll
+    for (int i = 0; i < DA; ++i) {
+        const int blk = wid * DA + i;
+        const int row = blk < NA ? 2 * blk + (lane >> 5) : (lane >> 5);
+        aoffs[i] = static_cast<uint32_t>(min(row, M - 1)) * static_cast<uint32_t>(K) +
+                   16u * static_cast<uint32_t>((lane & 31) ^ (row & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+        const int blk = wid * DB + i;
+        const int row = blk < NB ? 4 * blk + (lane >> 4) : (lane >> 4);
+        boffs[i] = static_cast<uint32_t>(min(n0 + row, N - 1) - n0) * static_cast<uint32_t>(RB) +
+                   16u * static_cast<uint32_t>((lane & 15) ^ (row & 7));
+    }
+    const int8_t *bbase = codes + static_cast<int64_t>(n0) * RB;
+    const int nrow = n0 + 16 * wid + j;
+    const bool nvalid = nrow < N;
+    // bytes of groups 4 s .. 4 s + 3 of this lane's row: two aligned dwords
+    // (a row's scales are 2 G bytes, G a multiple of 4)
+    const uint32_t sc_row = static_cast<uint32_t>(min(nrow, N - 1)) * static_cast<uint32_t>(2 * G);
+
+    auto issue_stage = [&](int s) {
+        const int sc = min(s, NS - 1);
+        const int buf = s % NST;
+#pragma unroll
+        for (int i = 0; i < DA; ++i) {
+            const int blk = wu * DA + i;
+            const uint32_t dst = blk < NA ? lds_offset(&As[buf][0]) + 1024u * blk
+                                          : lds_offset(&Xs[0]) + 1024u * (blk - NA);
+            dma16(q + static_cast<int64_t>(sc) * RA, aoffs[i], dst);
+        }
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+            const int blk = wu * DB + i;
+            const uint32_t dst = blk < NB ? lds_offset(&Bs[buf][0]) + 1024u * blk
+                                          : lds_offset(&Xs[0]) + 1024u * (DA * NW - NA + blk - NB);
+            dma16(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
+        }
+        dma4(gscale, sc_row + 8u * sc, lds_offset(&Ss[buf][wu][0][0]));
+        dma4(gscale, sc_row + 8u * sc + 4u, lds_offset(&Ss[buf][wu][1][0]));
+    };
+
+    v4i P[MB];
+    float F[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        P[mb] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) F[mb][e] = 0.0f;
+    }
+    // token chunk 8 p + 2 q + h of row r sits at 512 r + 128 p + 16 ((2 q + h) ^ (r & 7))
+    int aoff[2][MB];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) aoff[h][mb] = RA * (16 * mb + j) + 16 * ((2 * qd + h) ^ (j & 7));
+    // weight run 4 p + q of row r sits at (256 r + 16 (q ^ (r & 7))) ^ 64 p
+    const int boff = kSlKC * (16 * wid + j) + 16 * (qd ^ (j & 7));
+
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p) issue_stage(p);
+    for (int s = 0; s < NS; ++s) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * DMA) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_stage(s + NST - 1);
+        const int buf = s % NST;
+        const int8_t *Ab = As[buf];
+        const int8_t *Bb = Bs[buf];
+        const uint32_t sw0 = Ss[buf][wid][0][j], sw1 = Ss[buf][wid][1][j];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            v4i lo, hi;
+            tbl4_decode16(*reinterpret_cast<const v4i *>(Bb + (boff ^ (64 * p))), lo, hi);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                v4i a[MB];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i *>(Ab + aoff[h][mb] + 128 * p);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    P[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[mb], h ? hi : lo, h ? P[mb] : v4i{0, 0, 0, 0},
+                                                                   0, 0, 0);
+            }
+            const uint32_t sw = (p < 2) ? sw0 : sw1;
+            const float sc = bf16_to_f32(static_cast<uint16_t>((sw >> (16 * (p & 1))) & 0xFFFFu));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) F[mb][e] += static_cast<float>(P[mb][e]) * sc;
+                if constexpr (WRITE_P) {
+                    const int g = 4 * s + p;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = 16 * mb + 4 * qd + e;
+                        if (m < M && nvalid) partials[(static_cast<int64_t>(m) * N + nrow) * G + g] = P[mb][e];
+                    }
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!nvalid) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 16 * mb + 4 * qd + e;
+            if (m < M) y[static_cast<int64_t>(m) * N + nrow] = F[mb][e] * (scale[m] * 0x1p-7f);
+        }
+}
+
 using Shape64 = SlShape<4, 8, 3>;     // 33..64 tokens: 128 rows, 3 stages of 48 KiB
-using Shape128 = SlShape<8, 9, 2>;    // 65..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+using Shape128 = SlShape<8, 9, 2>;
+using ShapeT16 = SlShape<1, 9, 3>;   // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB    // 65..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+
+template <class S>
+hipError_t launch_tbl4_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
+                         int32_t *P, hipStream_t st) {
+    const int64_t grid = (w.N + S::BN - 1) / S::BN;
+    auto kern = P ? skinny_lds_tbl4_kernel<S, true> : skinny_lds_tbl4_kernel<S, false>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(64 * S::NW), 0, st, q, s, w.codes,
+                       w.gscale, y, P, static_cast<int>(M), static_cast<int>(w.N), static_cast<int>(w.K));
+    return hipGetLastError();
+}
 
 template <int FMT, class S>
 hipError_t launch_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
@@ -249,8 +409,18 @@ int lds_cu_count() {
 // for the register-streaming kernel; the 34816-row trunk at 33..64 tokens
 // (272 workgroups, 53%) 55-59 us against 40-43 us, so that shape keeps the
 // other kernel; at 112..128 tokens the 144-row workgroups (242, one round)
-// beat it by 1-4%, at 65..96 tokens (padded to 128) they lose.
+// beat it by 1-4%, at 65..96 tokens (padded to 128) they lose.  Codebook
+// format, 16 tokens on the 34816-row drafter linear (242 workgroups): 26.7 us
+// against 31.1 us.
 bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
+    if (w.fmt == 2) {
+        if (M < 9 || M > 16 || w.K % (2 * kSlKC) != 0) return false;
+        const int cus = lds_cu_count();
+        if (cus <= 0) return false;
+        const int64_t wgs = (w.N + ShapeT16::BN - 1) / ShapeT16::BN;
+        const int64_t rounds = (wgs + cus - 1) / cus;
+        return wgs * 100 >= 85 * rounds * cus;
+    }
     if (w.K % kSlKC != 0) return false;
     if (w.fmt == kFmtU8) {
         if (w.N * (w.K / 256) < 4) return false;
@@ -270,6 +440,7 @@ bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
 
 hipError_t launch_skinny_lds(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                              int32_t *partials, hipStream_t st) {
+    if (w.fmt == 2) return launch_tbl4_t<ShapeT16>(q, s, w, y, M, partials, st);
     if (M <= 64)
         return w.fmt == kFmtU8 ? launch_t<0, Shape64>(q, s, w, y, M, partials, st)
                                : launch_t<1, Shape64>(q, s, w, y, M, partials, st);

@@ -57,6 +57,22 @@ def test_tbl4_layer_partials_and_outputs(torch, M, K, N):
     rows_close(y.cpu().numpy(), oracle.epilogue(Pr, s, TBL, inp.gscale, None))
 
 
+# 9..16 tokens on enough weight rows (144-row workgroups filling >= 85% of a
+# round on a 256-CU MI355X) take the kernel that stages both operands through
+# LDS: ragged last workgroups, one and many stages of K, 9 and 16 tokens.
+@pytest.mark.parametrize("M,K,N", [(16, 512, 33000), (9, 1024, 31500), (12, 5120, 34816), (16, 2560, 36000)])
+def test_tbl4_lds_path(torch, M, K, N):
+    inp = W.make(M, K, N, TBL, seed=M * 5 + K + N)
+    q, s = oracle.quant_act_i8(inp.x)
+    w = weight(torch, inp)
+    y, P = B.w8a8_gemv(dev(torch, q), dev(torch, s), w, partials=True)
+    Pr = oracle.group_partials(q, inp.qw, TBL)
+    assert np.array_equal(P.cpu().numpy(), Pr)
+    rows_close(y.cpu().numpy(), oracle.epilogue(Pr, s, TBL, inp.gscale, None))
+    y2, _ = B.w8a8_gemv(dev(torch, q), dev(torch, s), w)          # production path, no partials
+    assert np.array_equal(y2.cpu().numpy(), y.cpu().numpy())
+
+
 @pytest.mark.parametrize("M", [1, 3, 16])
 def test_tbl4_whole_layer(torch, M):
     inp = W.make(M, 5120, 200, TBL, seed=90 + M)

@@ -8,13 +8,16 @@
 // of int8 activation codes times int8 weight codes per K group (256 with a u8
 // scale and a bf16 row scale, or 128 with a bf16 scale for the head), folded
 // per group into f32, then y = s_m * (r_n) * 2^-7 * sum_g scale[n][g] * P.
+// The drafter's format (table row "Speculator") stores 4-bit indices into a
+// 16-level integer table with a bf16 scale per 128; they are expanded to the
+// table's int8 values in registers and contracted the same way.
 //
 // A workgroup owns 16 weight rows per wave and all tokens (see SlShape).  K
 // is walked in 256-byte stages through an LDS ring filled by direct
 // global -> LDS 16-byte loads: one load instruction covers four rows x 256
 // contiguous bytes (the weight stream is the cost, and it streams fastest in
 // long runs per row), activation rows likewise.  Wave w computes its 16
-// weight rows against the 64 token rows with v_mfma_i32_16x16x64_i8 (A =
+// weight rows against all (padded) token rows with v_mfma_i32_16x16x64_i8 (A =
 // tokens, B = weights; lane j + 16 q holds chunk 4 kk + q of row j for k-step
 // kk, on both operands, so each matrix op sums the 64 products of its
 // k-step).  Each group's partials are folded into f32 when the group ends.

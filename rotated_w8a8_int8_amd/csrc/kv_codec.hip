@@ -84,8 +84,11 @@ __device__ __forceinline__ float code_div(float x, float s) {
 }
 __device__ __forceinline__ float code_rcp(float x, float rs, bool &near) {
     const float t = x * rs;
-    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
-    return fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+    const float r = __builtin_rintf(t);
+    // within 2^-13 of a half-integer <=> farther than 1/2 - 2^-13 from the
+    // nearest integer; t - r is exact (Sterbenz: r is 0, or within a factor 2 of t)
+    near = near || fabsf(t - r) > 0.5f - 0x1p-13f;
+    return fminf(fmaxf(r, -127.0f), 127.0f);
 }
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
     return (static_cast<uint32_t>(static_cast<int>(a)) & 0xFFu) |

@@ -85,8 +85,11 @@ __device__ __forceinline__ float wq_code(float w, float d) {
 // normal range [2^-120, 2^120], where 1/d is finite and normal.
 __device__ __forceinline__ float wq_code_rcp(float w, float rd, bool &near) {
     const float t = w * rd;
-    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
-    return fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+    const float r = __builtin_rintf(t);
+    // within 2^-13 of a half-integer <=> farther than 1/2 - 2^-13 from the
+    // nearest integer; t - r is exact (Sterbenz: r is 0, or within a factor 2 of t)
+    near = near || fabsf(t - r) > 0.5f - 0x1p-13f;
+    return fminf(fmaxf(r, -127.0f), 127.0f);
 }
 
 // (w - d q)^2 in f64; d q is exact in f32 (at most 16 + 7 significant bits)

@@ -93,8 +93,12 @@ __device__ __forceinline__ uint32_t pack4(float4 v, float s) {
 // [2^-120, 2^120] (1/s finite and normal).
 __device__ __forceinline__ float quant1_rcp(float v, float rs, bool &near) {
     const float t = v * rs;
-    near = near || fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
-    return __builtin_rintf(t);
+    const float r = __builtin_rintf(t);
+    // t lies within 2^-13 of a half-integer exactly when its distance to the
+    // nearest integer exceeds 1/2 - 2^-13; t - r is exact (Sterbenz: r is 0,
+    // or within a factor 2 of t)
+    near = near || fabsf(t - r) > 0.5f - 0x1p-13f;
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack4_rcp(float4 v, float s, float rs) {

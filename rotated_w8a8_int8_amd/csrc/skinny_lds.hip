@@ -40,12 +40,14 @@ constexpr int kFmtU8 = 0;
 constexpr int kSlKC = 256;                         // K bytes per stage
 
 // A workgroup shape: MB blocks of 16 tokens, NW waves of 16 weight rows, NST
-// stages in the LDS ring.  Each wave issues the same number of 1 KiB direct
+// stages in the LDS ring, NT: weight loads nontemporal (each weight byte is
+// read once per call; measured per shape, see the shapes below).  Each wave issues the same number of 1 KiB direct
 // loads per stage (the explicit waits count them); where a stage's blocks do
 // not split evenly over the waves, the remainder loads a valid block again
 // into a spare LDS area nobody reads.
-template <int MB_, int NW_, int NST_> struct SlShape {
+template <int MB_, int NW_, int NST_, bool NT_> struct SlShape {
     static constexpr int MB = MB_, NW = NW_, NST = NST_;
+    static constexpr bool NT = NT_;                                // weight loads nontemporal
     static constexpr int MP = 16 * MB, BN = 16 * NW;
     static constexpr int A = MP * kSlKC, B = BN * kSlKC;           // bytes per stage
     static constexpr int NA = A / 1024, NB = B / 1024;             // 1 KiB blocks per stage
@@ -55,6 +57,21 @@ template <int MB_, int NW_, int NST_> struct SlShape {
 };
 
 __device__ __forceinline__ int sl_addr(int row, int c) { return 256 * row + 16 * (c ^ (row & 7)); }
+
+// dma16 with the nontemporal cache policy (global_load_lds_dwordx4 ... nt)
+__device__ __forceinline__ void dma16nt(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(sbase), "{m0}"(lds)
+        : "memory");
+}
+template <bool NT>
+__device__ __forceinline__ void dma16_w(const void *sbase, uint32_t voff, uint32_t lds) {
+    if constexpr (NT) dma16nt(sbase, voff, lds);
+    else dma16(sbase, voff, lds);
+}
 
 template <int FMT, class S, bool WRITE_P>
 __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
             const int blk = wu * DB + i;
             const uint32_t dst = blk < S::NB ? lds_offset(&Bs[buf][0]) + 1024u * blk
                                              : lds_offset(&Xs[0]) + 1024u * (DA * S::NW - S::NA + blk - S::NB);
-            dma16(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
+            dma16_w<S::NT>(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
         }
         dma4(gscale, static_cast<uint32_t>(sc_dword(sc)), lds_offset(&Ss[buf][wu][0]));
     };
@@ -287,7 +304,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
             const int blk = wu * DB + i;
             const uint32_t dst = blk < NB ? lds_offset(&Bs[buf][0]) + 1024u * blk
                                           : lds_offset(&Xs[0]) + 1024u * (DA * NW - NA + blk - NB);
-            dma16(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
+            dma16_w<S::NT>(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
         }
         dma4(gscale, sc_row + 8u * sc, lds_offset(&Ss[buf][wu][0][0]));
         dma4(gscale, sc_row + 8u * sc + 4u, lds_offset(&Ss[buf][wu][1][0]));
@@ -363,9 +380,12 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
         }
 }
 
-using Shape64 = SlShape<4, 8, 3>;     // 33..64 tokens: 128 rows, 3 stages of 48 KiB
-using Shape128 = SlShape<8, 9, 2>;
-using ShapeT16 = SlShape<1, 9, 3>;   // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB    // 65..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+// Nontemporal weight loads: 128 tokens 53.6 -> 49.4 us (34816 rows), codebook
+// 16 tokens 26.8 -> 25.0 us; 64 tokens on the 152064-row head 188.9 -> 190.3 us,
+// so that shape keeps plain loads.
+using Shape64 = SlShape<4, 8, 3, false>;    // 33..64 tokens: 128 rows, 3 stages of 48 KiB
+using Shape128 = SlShape<8, 9, 2, true>;    // 112..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+using ShapeT16 = SlShape<1, 9, 3, true>;    // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB
 
 template <class S>
 hipError_t launch_tbl4_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,

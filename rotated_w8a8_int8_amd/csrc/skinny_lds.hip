@@ -41,13 +41,15 @@ constexpr int kSlKC = 256;                         // K bytes per stage
 
 // A workgroup shape: MB blocks of 16 tokens, NW waves of 16 weight rows, NST
 // stages in the LDS ring, NT: weight loads nontemporal (each weight byte is
-// read once per call; measured per shape, see the shapes below).  Each wave issues the same number of 1 KiB direct
+// read once per call), NTY: output stores nontemporal; both measured per
+// shape, see the shapes below.  Each wave issues the same number of 1 KiB direct
 // loads per stage (the explicit waits count them); where a stage's blocks do
 // not split evenly over the waves, the remainder loads a valid block again
 // into a spare LDS area nobody reads.
-template <int MB_, int NW_, int NST_, bool NT_> struct SlShape {
+template <int MB_, int NW_, int NST_, bool NT_, bool NTY_> struct SlShape {
     static constexpr int MB = MB_, NW = NW_, NST = NST_;
     static constexpr bool NT = NT_;                                // weight loads nontemporal
+    static constexpr bool NTY = NTY_;                              // output stores nontemporal
     static constexpr int MP = 16 * MB, BN = 16 * NW;
     static constexpr int A = MP * kSlKC, B = BN * kSlKC;           // bytes per stage
     static constexpr int NA = A / 1024, NB = B / 1024;             // 1 KiB blocks per stage
@@ -228,7 +230,11 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int m = 16 * mb + 4 * qd + e;
-            if (m < M) y[static_cast<int64_t>(m) * N + nrow] = F[mb][e] * (scale[m] * rn);
+            if (m < M) {
+                const float v = F[mb][e] * (scale[m] * rn);
+                if constexpr (S::NTY) __builtin_nontemporal_store(v, &y[static_cast<int64_t>(m) * N + nrow]);
+                else y[static_cast<int64_t>(m) * N + nrow] = v;
+            }
         }
 }
 
@@ -382,10 +388,13 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
 
 // Nontemporal weight loads: 128 tokens 53.6 -> 49.4 us (34816 rows), codebook
 // 16 tokens 26.8 -> 25.0 us; 64 tokens on the 152064-row head 188.9 -> 190.3 us,
-// so that shape keeps plain loads.
-using Shape64 = SlShape<4, 8, 3, false>;    // 33..64 tokens: 128 rows, 3 stages of 48 KiB
-using Shape128 = SlShape<8, 9, 2, true>;    // 112..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
-using ShapeT16 = SlShape<1, 9, 3, true>;    // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB
+// so that shape keeps plain loads.  Nontemporal output stores: the head at 64
+// tokens 189.0 -> 170.7 us (its 39 MB of outputs no longer displace the token
+// rows every workgroup re-reads); 128 tokens 49.5 -> 50.0 us, codebook 16
+// tokens unchanged, so those keep plain stores.
+using Shape64 = SlShape<4, 8, 3, false, true>;    // 33..64 tokens: 128 rows, 3 stages of 48 KiB
+using Shape128 = SlShape<8, 9, 2, true, false>;   // 112..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+using ShapeT16 = SlShape<1, 9, 3, true, false>;   // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB
 
 template <class S>
 hipError_t launch_tbl4_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,

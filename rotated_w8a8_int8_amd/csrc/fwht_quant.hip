@@ -148,8 +148,12 @@ hipError_t launch_quant_act(const float *x, int8_t *q, float *s, int64_t M, int6
     const int nblk = static_cast<int>(K / 128);
     const int Ki = static_cast<int>(K);
     // Few tokens, or long rows: 16 waves per token (4 blocks per wave per
-    // step) so each token finishes in few steps.  Many tokens: 4 waves each.
+    // step) so each token finishes in few steps, 8 waves when the row holds
+    // at most 64 blocks (K = 5120: 40 blocks, where 16 waves leave 6 of them
+    // without work).  Many tokens: 4 waves each.
     const int niter4 = (nblk + 15) / 16;
+    if (M < 256 && nblk <= 32) return launch_quant_t<8, 1>(x, q, s, M, Ki, rotate, st);
+    if (M < 256 && nblk <= 64) return launch_quant_t<8, 2>(x, q, s, M, Ki, rotate, st);
     if (M < 256 || niter4 > 12) {
         const int niter = (nblk + 63) / 64;
         if (niter <= 1) return launch_quant_t<16, 1>(x, q, s, M, Ki, rotate, st);

@@ -84,7 +84,7 @@ def test_fwht_integer_inputs_exact_hadamard(torch):
 # ------------------------------------------------------------ quantisation --
 
 QUANT_SHAPES = [(1, 128), (1, 5120), (2, 384), (17, 1024), (3, 17408), (300, 5120), (260, 17408),
-                (1, 65536), (2, 32768)]
+                (1, 65536), (2, 32768), (5, 4096), (120, 4224), (64, 8192)]
 
 
 @pytest.mark.parametrize("M,K", QUANT_SHAPES)

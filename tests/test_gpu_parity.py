@@ -177,6 +177,7 @@ def test_gemv_m_sweep(torch, M):
 @pytest.mark.parametrize("M,K,N,fmt", [(33, 256, 30000, 0), (48, 512, 30001, 0), (64, 2048, 28000, 1),
                                        (40, 256, 65466, 0), (64, 768, 30100, 1), (128, 256, 33000, 0),
                                        (120, 512, 34000, 1), (112, 256, 31400, 0),
+                                       (120, 1280, 31300, 0), (128, 768, 36000, 0),
                                        (64, 256, 5, 0), (50, 384, 70, 1)])
 def test_gemv_lds_path_shapes(torch, M, K, N, fmt):
     inp = W.make(M, K, N, fmt, seed=11 * M + K + N)

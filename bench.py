@@ -131,8 +131,8 @@ def lds_kernel_applies(wl, cus=256):
     """Whether the M <= 128 path runs the LDS-staged kernel for this workload on
     a part with `cus` compute units (the library's own rule: 33..64 or
     112..128 tokens in the int8 formats, 9..16 tokens in the codebook format,
-    workgroups of 128 or 144 weight rows filling at least 85% of their
-    rounds)."""
+    workgroups of 128 (trunk, 33..64 tokens), 208 (head, 33..64) or 144 weight
+    rows filling at least 85% of their rounds)."""
     if wl.fmt == 2:
         if not (9 <= wl.M <= 16) or wl.K % 512:
             return False
@@ -140,7 +140,7 @@ def lds_kernel_applies(wl, cus=256):
     elif wl.K % 256 or not (wl.fmt == 0 or (wl.fmt == 1 and (wl.K // 128) % 2 == 0)):
         return False
     elif 33 <= wl.M <= 64:
-        bn = 128
+        bn = 128 if wl.fmt == 0 else 208
     elif 112 <= wl.M <= 128:
         bn = 144
     else:

@@ -387,13 +387,18 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
 }
 
 // Nontemporal weight loads: 128 tokens 53.6 -> 49.4 us (34816 rows), codebook
-// 16 tokens 26.8 -> 25.0 us; 64 tokens on the 152064-row head 188.9 -> 190.3 us,
-// so that shape keeps plain loads.  Nontemporal output stores: the head at 64
-// tokens 189.0 -> 170.7 us (its 39 MB of outputs no longer displace the token
-// rows every workgroup re-reads); 128 tokens 49.5 -> 50.0 us, codebook 16
-// tokens unchanged, so those keep plain stores.
-using Shape64 = SlShape<4, 8, 3, false, true>;    // 33..64 tokens: 128 rows, 3 stages of 48 KiB
+// 16 tokens 26.8 -> 25.0 us; 64 tokens on the 152064-row head with the 128-row
+// shape 188.9 -> 190.3 us, so that shape keeps plain loads.  Nontemporal output
+// stores: the head at 64 tokens 189.0 -> 170.7 us (its 39 MB of outputs no
+// longer displace the token rows every workgroup re-reads); 128 tokens 49.5 ->
+// 50.0 us, codebook 16 tokens unchanged, so those keep plain stores.  The head
+// format at 33..64 tokens takes 208-row workgroups: 731 on the 152064-row head,
+// 2.86 rounds, against 1188 (4.64 rounds) of 128 rows, whose last round leaves
+// a third of the CUs idle; 169.9 -> 165.8 us with plain loads, 159.5 us with
+// nontemporal ones (160-row workgroups 175.8 us, 112-row 183.1 us).
+using Shape64 = SlShape<4, 8, 3, false, true>;    // trunk format, 33..64 tokens: 128 rows, 3 stages of 48 KiB
 using Shape128 = SlShape<8, 9, 2, true, false>;   // 112..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
+using ShapeH64 = SlShape<4, 13, 2, true, true>;   // head format, 33..64 tokens: 208 rows, 2 stages of 68 KiB (+10 KiB spare)
 using ShapeT16 = SlShape<1, 9, 3, true, false>;   // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB
 
 template <class S>
@@ -437,8 +442,8 @@ int lds_cu_count() {
 // A CU holds one of these workgroups at a time (LDS), so the kernel takes
 // whole rounds of workgroups; it is used only where its workgroups fill at
 // least 85% of their rounds.  Measured on MI355X (256 CUs, K = 5120): the
-// 152064-row head at 64 tokens (1188 workgroups, 93%) 189 us against 208 us
-// for the register-streaming kernel; the 34816-row trunk at 33..64 tokens
+// 152064-row head at 64 tokens (128-row workgroups: 1188, 93%) 189 us against
+// 208 us for the register-streaming kernel; the 34816-row trunk at 33..64 tokens
 // (272 workgroups, 53%) 55-59 us against 40-43 us, so that shape keeps the
 // other kernel; at 112..128 tokens the 144-row workgroups (242, one round)
 // beat it by 1-4%, at 65..96 tokens (padded to 128) they lose.  Codebook
@@ -460,7 +465,7 @@ bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
         return false;
     }
     int64_t bn;
-    if (M >= 33 && M <= 64) bn = Shape64::BN;
+    if (M >= 33 && M <= 64) bn = w.fmt == kFmtU8 ? Shape64::BN : ShapeH64::BN;
     else if (M >= 112 && M <= 128) bn = Shape128::BN;
     else return false;
     const int cus = lds_cu_count();
@@ -475,7 +480,7 @@ hipError_t launch_skinny_lds(const int8_t *q, const float *s, const WeightArgs &
     if (w.fmt == 2) return launch_tbl4_t<ShapeT16>(q, s, w, y, M, partials, st);
     if (M <= 64)
         return w.fmt == kFmtU8 ? launch_t<0, Shape64>(q, s, w, y, M, partials, st)
-                               : launch_t<1, Shape64>(q, s, w, y, M, partials, st);
+                               : launch_t<1, ShapeH64>(q, s, w, y, M, partials, st);
     return w.fmt == kFmtU8 ? launch_t<0, Shape128>(q, s, w, y, M, partials, st)
                            : launch_t<1, Shape128>(q, s, w, y, M, partials, st);
 }

@@ -169,15 +169,18 @@ def test_gemv_m_sweep(torch, M):
 
 
 # The kernel that stages both operands through LDS runs 33..64 and 112..128
-# tokens in the int8 formats where its workgroups (128 or 144 weight rows)
-# fill at least 85% of their rounds over the CUs; on a 256-CU MI355X these
-# shapes take it: ragged last workgroups, one and two rounds, one and many
-# stages of K, both formats.  Small weights and the head format with an odd
-# number of groups take the register-streaming kernel (last two cases).
+# tokens in the int8 formats where its workgroups (128 trunk or 208 head rows
+# for 33..64 tokens, 144 for 112..128) fill at least 85% of their rounds over
+# the CUs; on a 256-CU MI355X these shapes take it: ragged last workgroups,
+# one and two rounds, one and many stages of K, both formats.  The head format
+# at 64 tokens over 28000 and 30100 rows (135 and 145 workgroups), small
+# weights and the head format with an odd number of groups take the
+# register-streaming kernel.
 @pytest.mark.parametrize("M,K,N,fmt", [(33, 256, 30000, 0), (48, 512, 30001, 0), (64, 2048, 28000, 1),
                                        (40, 256, 65466, 0), (64, 768, 30100, 1), (128, 256, 33000, 0),
                                        (120, 512, 34000, 1), (112, 256, 31400, 0),
                                        (120, 1280, 31300, 0), (128, 768, 36000, 0),
+                                       (64, 768, 46000, 1), (40, 2048, 53000, 1), (33, 256, 100000, 1),
                                        (64, 256, 5, 0), (50, 384, 70, 1)])
 def test_gemv_lds_path_shapes(torch, M, K, N, fmt):
     inp = W.make(M, K, N, fmt, seed=11 * M + K + N)

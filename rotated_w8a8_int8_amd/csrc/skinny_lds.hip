@@ -25,9 +25,14 @@
 // direct load, so the only vector-memory operations of the loop are these
 // direct loads and the explicit waits below count them exactly.
 //
-// LDS: row r of a stage occupies 256 bytes; its logical 16-byte chunk c sits
-// in slot c ^ (r & 7), so the eight rows an operand read covers at a time hit
-// eight different 16-byte slots of a 128-byte bank line.
+// LDS: row r of a stage occupies 256 bytes (all 64 banks); its logical
+// 16-byte chunk c sits in slot c ^ (r & 15), so the 16 rows x 4 chunks of one
+// k-step's operand read spread over all 16 slots, four lanes a slot, the
+// fewest passes a 64-lane 16-byte read can take.  (The codebook kernel keeps
+// slot c ^ (r & 7).)  With r & 7, half the LDS cycles of these reads were bank
+// conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.50 on
+// both the 128-token trunk and the 64-token head); r & 15 took the 128-token
+// trunk shape from 50.3 to 47.9 us and left the head unchanged.
 #include <atomic>
 
 #include "rad_device.h"
@@ -58,7 +63,7 @@ template <int MB_, int NW_, int NST_, bool NT_, bool NTY_> struct SlShape {
     static constexpr int DMA = DA + DB + 1;                        // + the scale dword load
 };
 
-__device__ __forceinline__ int sl_addr(int row, int c) { return 256 * row + 16 * (c ^ (row & 7)); }
+__device__ __forceinline__ int sl_addr(int row, int c) { return 256 * row + 16 * (c ^ (row & 15)); }
 
 // dma16 with the nontemporal cache policy (global_load_lds_dwordx4 ... nt)
 __device__ __forceinline__ void dma16nt(const void *sbase, uint32_t voff, uint32_t lds) {
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
 
     // ---- direct loads of one stage.  Block b of an operand holds its rows
     // 4 b .. 4 b + 3 (lane l: row 4 b + l / 16, slot l % 16, i.e. logical
-    // chunk (l % 16) ^ (row & 7)).  Rows past M or N repeat the last row
+    // chunk (l % 16) ^ (row & 15)).  Rows past M or N repeat the last row
     // (never stored); block numbers past the operand's re-load block 0.
     const int dr = lane >> 4, dslot = lane & 15;
     uint32_t aoffs[DA], boffs[DB];
@@ -108,14 +113,14 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
         const int blk = wid * DA + i;
         const int row = blk < S::NA ? 4 * blk + dr : dr;
         aoffs[i] = static_cast<uint32_t>(min(row, M - 1)) * static_cast<uint32_t>(K) +
-                   16u * static_cast<uint32_t>(dslot ^ (row & 7));
+                   16u * static_cast<uint32_t>(dslot ^ (row & 15));
     }
 #pragma unroll
     for (int i = 0; i < DB; ++i) {
         const int blk = wid * DB + i;
         const int row = blk < S::NB ? 4 * blk + dr : dr;
         boffs[i] = static_cast<uint32_t>(min(n0 + row, N - 1) - n0) * static_cast<uint32_t>(K) +
-                   16u * static_cast<uint32_t>(dslot ^ (row & 7));
+                   16u * static_cast<uint32_t>(dslot ^ (row & 15));
     }
     const int8_t *bbase = codes + static_cast<int64_t>(n0) * K;
     // the scale dword of this lane's row for stage s: u8, byte n G + s; head,

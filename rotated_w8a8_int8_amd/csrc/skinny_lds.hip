@@ -47,10 +47,11 @@ constexpr int kSlKC = 256;                         // K bytes per stage
 // A workgroup shape: MB blocks of 16 tokens, NW waves of 16 weight rows, NST
 // stages in the LDS ring, NT: weight loads nontemporal (each weight byte is
 // read once per call), NTY: output stores nontemporal; both measured per
-// shape, see the shapes below.  Each wave issues the same number of 1 KiB direct
-// loads per stage (the explicit waits count them); where a stage's blocks do
-// not split evenly over the waves, the remainder loads a valid block again
-// into a spare LDS area nobody reads.
+// shape, see the shapes below.  In rings of three or more stages each wave
+// issues the same number of 1 KiB direct loads per stage (the explicit waits
+// count them): where a stage's blocks do not split evenly over the waves, the
+// remainder loads a valid block again into a spare LDS area nobody reads.
+// Two-stage rings wait for every load and skip those re-loads.
 template <int MB_, int NW_, int NST_, bool NT_, bool NTY_> struct SlShape {
     static constexpr int MB = MB_, NW = NW_, NST = NST_;
     static constexpr bool NT = NT_;                                // weight loads nontemporal
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;       // bytes per group scale
     __shared__ __attribute__((aligned(1024))) int8_t As[NST][S::A];
     __shared__ __attribute__((aligned(1024))) int8_t Bs[NST][S::B];
-    __shared__ __attribute__((aligned(1024))) int8_t Xs[S::SPARE > 0 ? S::SPARE * 1024 : 16];
+    __shared__ __attribute__((aligned(1024))) int8_t Xs[S::SPARE > 0 && NST > 2 ? S::SPARE * 1024 : 16];
     __shared__ __attribute__((aligned(256))) uint32_t Ss[NST][S::NW][64];
 
     const int lane = threadIdx.x & 63;
@@ -135,7 +136,10 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     auto sc_dword = [&](int s) -> int64_t { return min(sc_byte(s) & ~static_cast<int64_t>(3), sc_last); };
 
     // stages past the end re-load the last one into a buffer nobody reads
-    // again, so every wait count below is uniform
+    // again, so every wait count below is uniform.  With two stages each wait
+    // is for all of a wave's loads, so the spare re-loads that even out the
+    // waves' counts are skipped (1.2% on both the 128-token trunk and the
+    // 64-token head shapes once the LDS reads were conflict-free).
     auto issue_stage = [&](int s) {
         const int sc = min(s, NS - 1);
         const int buf = s % NST;
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
 #pragma unroll
         for (int i = 0; i < DA; ++i) {
             const int blk = wu * DA + i;
+            if (NST == 2 && blk >= S::NA) continue;
             const uint32_t dst = blk < S::NA ? lds_offset(&As[buf][0]) + 1024u * blk
                                              : lds_offset(&Xs[0]) + 1024u * (blk - S::NA);
             dma16(q + static_cast<int64_t>(sc) * kSlKC, aoffs[i], dst);
@@ -151,6 +156,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
 #pragma unroll
         for (int i = 0; i < DB; ++i) {
             const int blk = wu * DB + i;
+            if (NST == 2 && blk >= S::NB) continue;
             const uint32_t dst = blk < S::NB ? lds_offset(&Bs[buf][0]) + 1024u * blk
                                              : lds_offset(&Xs[0]) + 1024u * (DA * S::NW - S::NA + blk - S::NB);
             dma16_w<S::NT>(bbase + static_cast<int64_t>(sc) * kSlKC, boffs[i], dst);
@@ -402,8 +408,8 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
 // a third of the CUs idle; 169.9 -> 165.8 us with plain loads, 159.5 us with
 // nontemporal ones (160-row workgroups 175.8 us, 112-row 183.1 us).
 using Shape64 = SlShape<4, 8, 3, false, true>;    // trunk format, 33..64 tokens: 128 rows, 3 stages of 48 KiB
-using Shape128 = SlShape<8, 9, 2, true, false>;   // 112..128 tokens: 144 rows, 2 stages of 68 KiB (+4 KiB spare)
-using ShapeH64 = SlShape<4, 13, 2, true, true>;   // head format, 33..64 tokens: 208 rows, 2 stages of 68 KiB (+10 KiB spare)
+using Shape128 = SlShape<8, 9, 2, true, false>;   // 112..128 tokens: 144 rows, 2 stages of 68 KiB
+using ShapeH64 = SlShape<4, 13, 2, true, true>;   // head format, 33..64 tokens: 208 rows, 2 stages of 68 KiB
 using ShapeT16 = SlShape<1, 9, 3, true, false>;   // codebook format, 9..16 tokens: 144 rows, 3 stages of 44 KiB
 
 template <class S>

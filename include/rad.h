@@ -84,6 +84,14 @@ enum rad_format {
 #define RAD_GEMV_MAX_M 128
 /* Largest K that rad_quant_weight_i8 accepts (a rotated row is held on chip). */
 #define RAD_QUANT_WEIGHT_MAX_K 32768
+/* Largest K that the contraction calls (rad_w8a8_gemv, rad_w8a8_gemm,
+   rad_w8a8_linear, rad_w8a8_rescore) accept: the kernels address a tile of
+   up to 256 weight or token rows with 32-bit byte offsets row * K + column.
+   The same calls also return RAD_E_RANGE when the group-scale array
+   (N * (K / group width) * scale size) reaches 2^31 bytes, when a buffer's
+   byte count does not fit int64, or, for more than RAD_GEMV_MAX_M tokens,
+   when the output has 2^31 or more tiles of 256 x 128. */
+#define RAD_LINEAR_MAX_K 16777216
 
 /*
  * A quantised weight in the rotated domain.  Codes are int8 in -127..127 and

@@ -32,6 +32,7 @@ GROUP_WIDTH = {RAD_FMT_U8G256_BF16ROW: 256, RAD_FMT_BF16G128: 128, RAD_FMT_TBL4_
 RAD_QUANT_MAX_K = 65536
 RAD_GEMV_MAX_M = 128
 RAD_QUANT_WEIGHT_MAX_K = 32768
+RAD_LINEAR_MAX_K = 16777216
 
 EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
            "rad_quant_weight_i8", "rad_kv_quant_i8", "rad_kv_dequant_i8", "rad_w8a8_rescore",
@@ -114,6 +115,29 @@ def _dev(t, dtype, name):
     return t
 
 
+def _bits16_dev(t, name):
+    """A contiguous GPU tensor of 16-bit bit patterns (bf16 or f16 values)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor" % name)
+    if t.dtype not in (torch.int16, torch.uint16, torch.bfloat16, torch.float16):
+        raise TypeError("%s must hold 16-bit values, got %s" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _same_device(ref, *named):
+    for t, name in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, ref.device))
+
+
 def _stream(t):
     return _torch().cuda.current_stream(t.device).cuda_stream
 
@@ -140,14 +164,28 @@ class W8A8Weight:
         return int(self.codes.shape[1]) * (2 if self.fmt == RAD_FMT_TBL4_BF16G128 else 1)
 
     def desc(self) -> WeightDesc:
+        """The C descriptor, after checking every tensor's device, dtype,
+        contiguity and shape against the format (so no short or strided buffer
+        reaches a kernel)."""
         torch = _torch()
+        if self.fmt not in GROUP_WIDTH:
+            raise ValueError("unknown weight format %r" % (self.fmt,))
         _dev(self.codes, torch.uint8 if self.fmt == RAD_FMT_TBL4_BF16G128 else torch.int8, "codes")
+        if self.codes.dim() != 2:
+            raise ValueError("codes must be 2-D, got shape %s" % (tuple(self.codes.shape),))
+        G = self.K // GROUP_WIDTH[self.fmt]
         if self.fmt == RAD_FMT_U8G256_BF16ROW:
             _dev(self.gscale, torch.uint8, "gscale")
-        elif self.gscale.dtype not in (torch.int16, torch.uint16):
-            raise TypeError("gscale must hold bf16 bits (int16/uint16)")
-        if self.rscale is not None and self.rscale.dtype not in (torch.int16, torch.uint16):
-            raise TypeError("rscale must hold bf16 bits (int16/uint16)")
+            if self.rscale is None:
+                raise ValueError("the u8 format needs row scales (rscale)")
+            _bits16_dev(self.rscale, "rscale")
+            _shape(self.rscale, (self.N,), "rscale")
+        else:
+            _bits16_dev(self.gscale, "gscale")
+            if self.rscale is not None:
+                raise ValueError("this format takes no row scales (rscale must be None)")
+        _shape(self.gscale, (self.N, G), "gscale")
+        _same_device(self.codes, (self.gscale, "gscale"), (self.rscale, "rscale"))
         return WeightDesc(self.codes.data_ptr(), self.gscale.data_ptr(),
                           None if self.rscale is None else self.rscale.data_ptr(),
                           self.N, self.K, self.fmt)
@@ -161,6 +199,8 @@ def fwht128(x, out=None):
     if out is None:
         out = torch.empty_like(x)
     _dev(out, torch.float32, "out")
+    _shape(out, x.shape, "out")
+    _same_device(x, (out, "out"))
     rows = x.numel() // K if K else 0
     _check(lib().rad_fwht128(x.data_ptr(), out.data_ptr(), rows, K, _stream(x)), "rad_fwht128")
     return out
@@ -177,6 +217,9 @@ def quant_act_i8(x, rotate: bool = True, q=None, scale=None):
         scale = torch.empty((M,), dtype=torch.float32, device=x.device)
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
+    _shape(q, (M, K), "q")
+    _shape(scale, (M,), "scale")
+    _same_device(x, (q, "q"), (scale, "scale"))
     _check(lib().rad_quant_act_i8(x.data_ptr(), q.data_ptr(), scale.data_ptr(), M, K,
                                   1 if rotate else 0, _stream(x)), "rad_quant_act_i8")
     return q, scale
@@ -186,21 +229,26 @@ def _linear_call(fn, name, q, scale, w: W8A8Weight, y, partials):
     torch = _torch()
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
+    d = w.desc()
+    if q.dim() != 2 or q.shape[1] != w.K:
+        raise ValueError("q has shape %s, weight has K=%d" % (tuple(q.shape), w.K))
     M = int(q.shape[0])
-    if q.shape[1] != w.K:
-        raise ValueError("q has K=%d, weight has K=%d" % (q.shape[1], w.K))
+    _shape(scale, (M,), "scale")
     if y is None:
         y = torch.empty((M, w.N), dtype=torch.float32, device=q.device)
     _dev(y, torch.float32, "y")
+    _shape(y, (M, w.N), "y")
     pp = None
+    G = w.K // GROUP_WIDTH[w.fmt]
     if partials is True:
-        partials = torch.empty((M, w.N, w.K // GROUP_WIDTH[w.fmt]), dtype=torch.int32, device=q.device)
+        partials = torch.empty((M, w.N, G), dtype=torch.int32, device=q.device)
     if partials is not None and partials is not False:
         _dev(partials, torch.int32, "partials")
+        _shape(partials, (M, w.N, G), "partials")
         pp = partials.data_ptr()
     else:
         partials = None
-    d = w.desc()
+    _same_device(q, (scale, "scale"), (w.codes, "codes"), (y, "y"), (partials, "partials"))
     _check(fn(q.data_ptr(), scale.data_ptr(), ctypes.byref(d), y.data_ptr(), M, pp, _stream(q)), name)
     return y, partials
 
@@ -232,6 +280,10 @@ def linear(x, w: W8A8Weight, q=None, scale=None, y=None):
     _dev(scale, torch.float32, "scale")
     _dev(y, torch.float32, "y")
     d = w.desc()
+    _shape(q, (M, K), "q")
+    _shape(scale, (M,), "scale")
+    _shape(y, (M, w.N), "y")
+    _same_device(x, (q, "q"), (scale, "scale"), (y, "y"), (w.codes, "codes"))
     _check(lib().rad_w8a8_linear(x.data_ptr(), q.data_ptr(), scale.data_ptr(), ctypes.byref(d),
                                  y.data_ptr(), M, _stream(x)), "rad_w8a8_linear")
     return y, q, scale
@@ -252,37 +304,30 @@ def quant_weight_i8(W, fmt: int, codes=None, gscale=None, rscale=None) -> W8A8We
         gscale = torch.empty((N, G), dtype=gdt, device=W.device)
     if rscale is None and fmt == RAD_FMT_U8G256_BF16ROW:
         rscale = torch.empty((N,), dtype=torch.int16, device=W.device)
-    _dev(codes, torch.uint8 if tbl else torch.int8, "codes")
-    if not (gscale.is_cuda and gscale.is_contiguous()):
-        raise TypeError("gscale must be a contiguous GPU tensor")
-    if rscale is not None and not (rscale.is_cuda and rscale.is_contiguous()):
-        raise TypeError("rscale must be a contiguous GPU tensor")
+    out = W8A8Weight(codes, gscale, rscale, fmt)
+    out.desc()                      # device, dtype, contiguity and shape of every output
+    _shape(codes, (N, K // 2 if tbl else K), "codes")
+    _same_device(W, (codes, "codes"))
     _check(lib().rad_quant_weight_i8(W.data_ptr(), codes.data_ptr(), gscale.data_ptr(),
                                      None if rscale is None else rscale.data_ptr(), N, K, fmt,
                                      _stream(W)), "rad_quant_weight_i8")
-    return W8A8Weight(codes, gscale, rscale, fmt)
-
-
-def _bits16(t, name):
-    torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
-        raise TypeError("%s must be a contiguous GPU tensor" % name)
-    if t.dtype not in (torch.int16, torch.uint16, torch.bfloat16, torch.float16):
-        raise TypeError("%s must hold 16-bit values" % name)
-    return t
+    return out
 
 
 def kv_quant_i8(x, codes=None, scale=None):
     """int8 KV-cache encode of bf16 rows ``x`` [rows][D]: returns (codes, f16 scales)."""
     torch = _torch()
-    _bits16(x, "x")
+    _bits16_dev(x, "x")
     rows, D = x.shape
     if codes is None:
         codes = torch.empty((rows, D), dtype=torch.int8, device=x.device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float16, device=x.device)
     _dev(codes, torch.int8, "codes")
-    _bits16(scale, "scale")
+    _bits16_dev(scale, "scale")
+    _shape(codes, (rows, D), "codes")
+    _shape(scale, (rows,), "scale")
+    _same_device(x, (codes, "codes"), (scale, "scale"))
     _check(lib().rad_kv_quant_i8(x.data_ptr(), codes.data_ptr(), scale.data_ptr(), rows, D, _stream(x)),
            "rad_kv_quant_i8")
     return codes, scale
@@ -292,11 +337,14 @@ def kv_dequant_i8(codes, scale, y=None):
     """Read an int8 KV cache back to bf16 [rows][D]."""
     torch = _torch()
     _dev(codes, torch.int8, "codes")
-    _bits16(scale, "scale")
+    _bits16_dev(scale, "scale")
     rows, D = codes.shape
+    _shape(scale, (rows,), "scale")
     if y is None:
         y = torch.empty((rows, D), dtype=torch.bfloat16, device=codes.device)
-    _bits16(y, "y")
+    _bits16_dev(y, "y")
+    _shape(y, (rows, D), "y")
+    _same_device(codes, (scale, "scale"), (y, "y"))
     _check(lib().rad_kv_dequant_i8(codes.data_ptr(), scale.data_ptr(), y.data_ptr(), rows, D,
                                    _stream(codes)), "rad_kv_dequant_i8")
     return y
@@ -308,13 +356,16 @@ def w8a8_rescore(q, scale, w: W8A8Weight, ids, y=None):
     _dev(q, torch.int8, "q")
     _dev(scale, torch.float32, "scale")
     _dev(ids, torch.int32, "ids")
+    d = w.desc()
     M, C = ids.shape
     if q.shape[0] != M or q.shape[1] != w.K:
         raise ValueError("q is %s, expected [%d, %d]" % (tuple(q.shape), M, w.K))
+    _shape(scale, (M,), "scale")
     if y is None:
         y = torch.empty((M, C), dtype=torch.float32, device=q.device)
     _dev(y, torch.float32, "y")
-    d = w.desc()
+    _shape(y, (M, C), "y")
+    _same_device(q, (scale, "scale"), (ids, "ids"), (y, "y"), (w.codes, "codes"))
     _check(lib().rad_w8a8_rescore(q.data_ptr(), scale.data_ptr(), ctypes.byref(d), ids.data_ptr(), C,
                                   y.data_ptr(), M, _stream(q)), "rad_w8a8_rescore")
     return y

@@ -367,6 +367,10 @@ hipError_t launch_gemm_t(const int8_t *q, const float *s, const WeightArgs &w, f
 
 }  // namespace
 
+bool gemm_grid_fits(int64_t M, int64_t N) {
+    return ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN) < (int64_t(1) << 31);
+}
+
 hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st) {
     const int64_t scale_bytes = w.N * (w.K / (w.fmt == kFmtU8 ? 256 : 128)) * (w.fmt == kFmtU8 ? 1 : 2);

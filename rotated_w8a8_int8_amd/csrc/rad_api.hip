@@ -6,6 +6,8 @@
 // pointers -> alignment -> aliasing.
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/rad.h"
 #include "rad_launch.h"
 
@@ -16,13 +18,29 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 struct Span {
     uintptr_t lo, hi;  // [lo, hi)
 };
+// [p, p + bytes), the end clamped to the top of the address space (no real
+// buffer wraps; the clamp only keeps the comparison below meaningful).
 Span span(const void *p, int64_t bytes) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Span{lo, lo + static_cast<uintptr_t>(bytes)};
+    const uintptr_t n = static_cast<uintptr_t>(bytes);
+    return Span{lo, n > UINTPTR_MAX - lo ? UINTPTR_MAX : lo + n};
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
 
 constexpr int64_t kI32Max = 2147483647;
+// Group-scale arrays are addressed with 32-bit byte offsets in the kernels.
+constexpr int64_t kMaxScaleBytes = int64_t(1) << 31;
+static_assert(int64_t(255) * RAD_LINEAR_MAX_K + 128 < (int64_t(1) << 32),
+              "a 256-row tile's lane offsets (row * K + chunk) fit 32 bits");
+
+// Product of non-negative sizes, or -1 when it does not fit int64 (no buffer
+// is that large, so such sizes are out of range).
+int64_t checked_mul(std::initializer_list<int64_t> xs) {
+    int64_t r = 1;
+    for (int64_t x : xs)
+        if (__builtin_mul_overflow(r, x, &r)) return -1;
+    return r;
+}
 static_assert(RAD_QUANT_WEIGHT_MAX_K == rad::kQuantWeightMaxK, "header and kernel agree on the largest K");
 
 int group_width(int32_t fmt) {
@@ -44,20 +62,24 @@ int check_linear(const int8_t *q, const float *scale, const rad_w8a8_weight *w, 
     if (w->fmt == RAD_FMT_U8G256_BF16ROW && !w->rscale) return RAD_E_FMT;
     if (w->fmt != RAD_FMT_U8G256_BF16ROW && w->rscale) return RAD_E_FMT;
     if (M < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
-    if (M > max_m || w->N > kI32Max || w->K > kI32Max) return RAD_E_RANGE;
+    if (M > max_m || w->N > kI32Max || w->K > RAD_LINEAR_MAX_K) return RAD_E_RANGE;
+    const int64_t N = w->N, K = w->K, G = K / gw;
+    const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
+    const int64_t qb = checked_mul({M, K}), yb = checked_mul({M, N, 4}), gb = checked_mul({N, G, esz}),
+                  pb = partials ? checked_mul({M, N, G, 4}) : 0;
+    if (qb < 0 || yb < 0 || gb < 0 || pb < 0 || gb >= kMaxScaleBytes) return RAD_E_RANGE;
+    if (M > RAD_GEMV_MAX_M && !rad::gemm_grid_fits(M, N)) return RAD_E_RANGE;
     if (M == 0 || w->N == 0) return 1;  // nothing to do
     if (!q || !scale || !y || !w->codes || !w->gscale) return RAD_E_NULL;
     if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(w->gscale, 4) ||
         (w->rscale && !aligned(w->rscale, 4)) || !aligned(scale, 4) || !aligned(y, 4) ||
         (partials && !aligned(partials, 4)))
         return RAD_E_ALIGN;
-    const int64_t N = w->N, K = w->K, G = K / gw;
-    const int esz = (w->fmt == RAD_FMT_U8G256_BF16ROW) ? 1 : 2;
-    const Span in[] = {span(q, M * K), span(scale, M * 4), span(w->codes, N * code_bytes(w->fmt, K)),
-                       span(w->gscale, N * G * esz),
+    const Span in[] = {span(q, qb), span(scale, M * 4), span(w->codes, N * code_bytes(w->fmt, K)),
+                       span(w->gscale, gb),
                        w->rscale ? span(w->rscale, N * 2) : Span{0, 0}};
-    const Span ys = span(y, M * N * 4);
-    const Span ps = partials ? span(partials, M * N * G * 4) : Span{0, 0};
+    const Span ys = span(y, yb);
+    const Span ps = partials ? span(partials, pb) : Span{0, 0};
     for (const Span &s : in) {
         if (overlap(ys, s)) return RAD_E_ALIAS;
         if (partials && overlap(ps, s)) return RAD_E_ALIAS;
@@ -180,8 +202,10 @@ int rad_w8a8_rescore(const int8_t *q, const float *scale, const rad_w8a8_weight 
     if (w->fmt != RAD_FMT_U8G256_BF16ROW && w->rscale) return RAD_E_FMT;
     if (w->fmt == RAD_FMT_TBL4_BF16G128) return RAD_E_FMT;       // int8 weights only
     if (M < 0 || C < 0 || w->N < 0 || w->K <= 0 || w->K % 128 != 0 || w->K % gw != 0) return RAD_E_SHAPE;
-    if (w->N > kI32Max || w->K > kI32Max || C > kI32Max || M > kI32Max || M * C >= (int64_t(1) << 33))
+    if (w->N > kI32Max || w->K > RAD_LINEAR_MAX_K || C > kI32Max || M > kI32Max ||
+        M * C >= (int64_t(1) << 33))
         return RAD_E_RANGE;
+    if (checked_mul({w->N, w->K / gw, 2}) >= kMaxScaleBytes) return RAD_E_RANGE;
     if (M == 0 || C == 0) return RAD_OK;
     if (!q || !scale || !ids || !y || !w->codes || !w->gscale) return RAD_E_NULL;
     if (!aligned(q, 16) || !aligned(w->codes, 16) || !aligned(w->gscale, 4) ||

@@ -45,5 +45,7 @@ hipError_t launch_kv_dequant(const int8_t *codes, const uint16_t *scale, uint16_
                              int64_t D, hipStream_t st);
 hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st);
+// Whether launch_gemm's grid (one workgroup per output tile) fits a launch.
+bool gemm_grid_fits(int64_t M, int64_t N);
 
 }  // namespace rad

@@ -46,7 +46,7 @@ def test_constants_match_header():
                  "RAD_FMT_BF16G128", "RAD_FMT_TBL4_BF16G128"):
         m = re.search(r"\b%s\s*=\s*(-?\d+)" % name, h)
         assert m and int(m.group(1)) == getattr(B, name), name
-    for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M", "RAD_QUANT_WEIGHT_MAX_K"):
+    for name in ("RAD_QUANT_MAX_K", "RAD_GEMV_MAX_M", "RAD_QUANT_WEIGHT_MAX_K", "RAD_LINEAR_MAX_K"):
         m = re.search(r"#define %s (\d+)" % name, h)
         assert m and int(m.group(1)) == getattr(B, name)
 
@@ -114,6 +114,17 @@ def test_linear_validation(name, max_m):
     if max_m is not None:
         assert call(desc(), M=max_m + 1) == B.RAD_E_RANGE
     assert call(desc(N=1 << 31)) == B.RAD_E_RANGE
+    # 32-bit lane offsets: K past the limit, a group-scale array of 2^31
+    # bytes, a buffer whose byte count overflows int64 (the partials), and a
+    # grid of 2^31 output tiles
+    assert call(desc(K=B.RAD_LINEAR_MAX_K + 256)) == B.RAD_E_RANGE
+    assert call(desc(K=1 << 62)) == B.RAD_E_RANGE
+    assert call(desc(N=1 << 24, K=256 * 128)) == B.RAD_E_RANGE
+    assert call(desc(N=(1 << 24) - 1, K=256 * 128, fmt=B.RAD_FMT_BF16G128, rscale=None)) \
+        == B.RAD_E_RANGE                                            # 2 bytes a head scale
+    if max_m is None:
+        assert call(desc(N=1 << 23, K=256 * 255), M=(1 << 31) - 1, p=E + 0x100000) == B.RAD_E_RANGE
+        assert call(desc(N=1 << 16), M=(1 << 31) - 1) == B.RAD_E_RANGE
     assert call(desc(), M=0, q=0, s=0, y=0) == B.RAD_OK              # empty batch
     assert call(desc(N=0, codes=0, gscale=0), q=0, s=0, y=0) == B.RAD_OK
     assert call(desc(), q=0) == B.RAD_E_NULL
@@ -217,6 +228,9 @@ def test_rescore_validation():
     assert call(desc(K=384)) == B.RAD_E_SHAPE
     assert call(desc(), C=-1) == B.RAD_E_SHAPE
     assert call(desc(), M=1 << 20, C=1 << 14) == B.RAD_E_RANGE
+    assert call(desc(K=B.RAD_LINEAR_MAX_K + 256)) == B.RAD_E_RANGE
+    assert call(desc(N=(1 << 24) - 1, K=256 * 128, fmt=B.RAD_FMT_BF16G128, rscale=None)) \
+        == B.RAD_E_RANGE
     assert call(desc(), M=0, q=0, s=0, ids=0, y=0) == B.RAD_OK
     assert call(desc(), C=0, ids=0, y=0) == B.RAD_OK
     assert call(desc(), ids=0) == B.RAD_E_NULL

@@ -9,8 +9,8 @@ partials carries a relative error near 1e-7 of the row norm.
 
 Small shapes span several tiles with ragged tails and are compared in full.
 The five workloads are run at full size in the launch configuration the
-benchmark uses; their codes are compared in full and their partials and
-outputs on sampled token rows that the oracle computes one by one.
+benchmark uses and compared on every token row: codes, scales, all group
+partials and all outputs (the prefill in chunks of 512 rows).
 """
 import numpy as np
 import pytest
@@ -289,19 +289,13 @@ def test_linear_zero_token(torch):
 
 # ------------------------------------------------------ full-size workloads --
 
-def sample_rows(M, n, seed):
-    if M <= n:
-        return np.arange(M)
-    rng = np.random.default_rng(seed)
-    pick = set([0, M - 1, M // 2]) | set(rng.choice(M, size=n, replace=False).tolist())
-    return np.array(sorted(pick))[:n + 3]
-
-
-@pytest.mark.parametrize("name,fn,nsample", [
-    ("tiny", "gemv", 4), ("decode_gate_up", "gemv", 1), ("verify_skinny", "gemv", 12),
-    ("vocab_head", "gemv", 6), ("prefill_down", "gemm", 10), ("tiny", "gemm", 4),
+@pytest.mark.parametrize("name,fn", [
+    ("tiny", "gemv"), ("decode_gate_up", "gemv"), ("verify_skinny", "gemv"), ("vocab_head", "gemv"),
+    ("tiny", "gemm"),
 ])
-def test_workload_full_size(torch, name, fn, nsample):
+def test_workload_full_size(torch, name, fn):
+    """Every token row of the workload: codes, scales, all group partials and
+    all outputs, in the benchmark's launch configuration."""
     wl = W.WORKLOADS[name]
     print("workload", name, fn, flush=True)
     inp = W.make_workload(name, seed=0)
@@ -314,13 +308,103 @@ def test_workload_full_size(torch, name, fn, nsample):
     w = weight(torch, inp)
     call = B.w8a8_gemv if fn == "gemv" else B.w8a8_gemm
     y, P = call(qd, sd, w, partials=True)
-    rows = sample_rows(wl.M, nsample, seed=1)
-    rows_t = torch.from_numpy(rows).cuda()
-    Ps = host(P.index_select(0, rows_t))
-    ys = host(y.index_select(0, rows_t))
+    Pr = oracle.group_partials(q, inp.qw, wl.fmt)
+    assert np.array_equal(host(P), Pr)
     del P
-    Pr = oracle.group_partials(q[rows], inp.qw, wl.fmt)
-    assert np.array_equal(Ps, Pr)
-    assert_rows_close(ys, oracle.epilogue(Pr, s[rows], wl.fmt, inp.gscale, inp.rscale))
+    y = host(y)
+    assert_rows_close(y, oracle.epilogue(Pr, s, wl.fmt, inp.gscale, inp.rscale))
+    del Pr
     y2, _ = call(qd, sd, w)                                 # the benchmark's launch
-    assert np.array_equal(host(y2.index_select(0, rows_t)), ys)
+    assert np.array_equal(host(y2).view(np.int32), y.view(np.int32))
+
+
+def test_prefill_full_size_every_row(torch):
+    """prefill_down (8192 x 17408 x 5120) on the GEMM: every code and scale,
+    then all 8192 x 5120 x 68 group partials and every output, compared in
+    chunks of 512 token rows against the oracle."""
+    wl = W.WORKLOADS["prefill_down"]
+    print("workload prefill_down gemm, every row", flush=True)
+    inp = W.make_workload("prefill_down", seed=0)
+    xd = dev(torch, inp.x)
+    qd, sd = B.quant_act_i8(xd)
+    q, s = oracle.quant_act_i8(inp.x)
+    assert np.array_equal(host(sd).view(np.int32), s.view(np.int32))
+    assert np.array_equal(host(qd), q)
+    del xd
+    w = weight(torch, inp)
+    y, P = B.w8a8_gemm(qd, sd, w, partials=True)
+    y2, _ = B.w8a8_gemm(qd, sd, w)                          # the benchmark's launch
+    assert torch.equal(y, y2)
+    del y
+    for m0 in range(0, wl.M, 512):
+        Pr = oracle.group_partials(q[m0:m0 + 512], inp.qw, wl.fmt)
+        assert np.array_equal(host(P[m0:m0 + 512]), Pr), "partials differ in rows %d.." % m0
+        yr = oracle.epilogue(Pr, s[m0:m0 + 512], wl.fmt, inp.gscale, inp.rscale)
+        assert_rows_close(host(y2[m0:m0 + 512]), yr)
+
+
+# Tile counts divisible by 8 take the GEMM's XCD slab order (each XCD gets a
+# contiguous run of tiles); the small shapes above do not.  8 x 8, 4 x 16 and
+# 16 x 8 tiles of 256 x 128, with several 4-tile slabs per XCD in the last.
+@pytest.mark.parametrize("M,K,N,fmt", [(2048, 512, 1024, 0), (1024, 768, 2048, 1), (4096, 256, 1000, 0)])
+def test_gemm_xcd_slab_order(torch, M, K, N, fmt):
+    inp = W.make(M, K, N, fmt, seed=M + K + N)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemm, inp)
+    Pr = oracle.group_partials(q, inp.qw, fmt)
+    assert np.array_equal(P, Pr)
+    assert_rows_close(y, oracle.epilogue(Pr, s, fmt, inp.gscale, inp.rscale))
+    y2, _ = B.w8a8_gemm(qd, sd, w)
+    assert np.array_equal(host(y2), y)
+
+
+# ------------------------------------------- tiny scales: division branches --
+
+def tiny_tokens(K, seed):
+    """Tokens whose scale amax/127 falls below 2^-120 (where the quantiser
+    divides instead of multiplying by the reciprocal), lands exactly on 2^-120
+    or just below it, is subnormal, or underflows to zero with amax > 0."""
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((5, K)).astype(np.float32)
+    rows = [(base[i] * np.float32(2.0 ** e)).astype(np.float32)
+            for i, e in enumerate((-118, -125, -131, -140, -146))]
+    c = np.float32(127.0 * 2.0 ** -120 / 128.0)
+    at_rot = np.zeros(K, np.float32)                  # rotated: (127 * 2^-120, 0, ...), s = 2^-120
+    at_rot[:128] = c
+    at_raw = (base[0] * np.float32(2.0 ** -130)).astype(np.float32)
+    at_raw[K // 2] = np.float32(-127.0 * 2.0 ** -120)  # unrotated amax 127 * 2^-120, s = 2^-120
+    for r in (at_rot, at_raw):
+        rows.append(r)
+        below = r.copy()                              # the next float below: s < 2^-120
+        i = 0 if r is at_rot else K // 2
+        below[i] = np.nextafter(below[i], np.float32(0))
+        if r is at_rot:
+            below[1:128] = below[0]
+        rows.append(below)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("K", [512, 5120, 17408])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_quant_tiny_scales_bit_exact(torch, K, rotate):
+    x = tiny_tokens(K, seed=K)
+    qr, sr = oracle.quant_act_i8(x, rotate=rotate)
+    assert np.any((sr > 0) & (sr < np.float32(2.0 ** -126)))             # subnormal scales occur
+    assert np.any(sr == np.float32(2.0 ** -120)) and np.any((sr > 0) & (sr < np.float32(2.0 ** -120)))
+    q, s = B.quant_act_i8(dev(torch, x), rotate=rotate)
+    assert np.array_equal(host(s).view(np.int32), sr.view(np.int32))
+    assert np.array_equal(host(q), qr)
+
+
+@pytest.mark.parametrize("K", [512, 5120])
+def test_fused_decode_tiny_scales(torch, K):
+    # one token: the fused kernel rotates and quantises with the division
+    inp = W.make(1, K, 300, 0, seed=K)
+    w = weight(torch, inp)
+    for x in tiny_tokens(K, seed=K + 1):
+        x = x[None, :]
+        y, q, s = B.linear(dev(torch, x), w)
+        qr, sr = oracle.quant_act_i8(x)
+        assert np.array_equal(host(s).view(np.int32), sr.view(np.int32))
+        assert np.array_equal(host(q), qr)
+        yr = oracle.linear(qr, sr, inp.qw, 0, inp.gscale, inp.rscale)
+        assert np.array_equal(host(y).view(np.int32), yr.view(np.int32))

@@ -6,8 +6,7 @@ take it with the same f32 and f64 operations in the same order (the pairwise
 tree of the search), so every decision, ties included, must agree exactly.
 Small shapes cover one to many groups, an odd number of head groups, both
 on-chip row sizes and the largest K; the full-size cases run at the weight
-shapes of the benchmark workloads and are compared on sampled rows, which the
-oracle quantises one by one.
+shapes of the benchmark workloads and are compared on every row.
 """
 import numpy as np
 import pytest
@@ -106,9 +105,41 @@ FULL = [("decode_gate_up", 34816, 5120, U8), ("prefill_down", 5120, 17408, U8),
 
 
 @pytest.mark.parametrize("name,N,K,fmt", FULL)
-def test_full_size_sampled_rows(torch, name, N, K, fmt):
+def test_full_size_every_row(torch, name, N, K, fmt):
+    print("weight quantiser", name, flush=True)
     Wf = W.make_float_weights(N, K, seed=35)
-    got = run(torch, Wf, fmt)
-    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(36).integers(0, N, 30)]))
-    want = oracle.quant_weight_i8(Wf[rows], fmt)
-    assert_same((got[0][rows], got[1][rows], None if got[2] is None else got[2][rows]), want)
+    assert_same(run(torch, Wf, fmt), oracle.quant_weight_i8(Wf, fmt))
+
+
+def extreme_weights(K, seed):
+    """Rows whose group scales d fall outside [2^-120, 2^120], where the
+    quantiser takes its codes from the division for the whole wave: tiny
+    rows (d below 2^-120, subnormal scales, scales that round to zero) and rows with
+    one 128-block of constant +-2^120, which rotates to +-2^127 and puts that
+    group's scale just above 2^120."""
+    Wf = W.make_float_weights(7, K, seed=seed)
+    Wf[0] *= np.float32(2.0 ** -115)
+    Wf[1] *= np.float32(2.0 ** -120)
+    Wf[2] *= np.float32(2.0 ** -122)
+    Wf[3] *= np.float32(2.0 ** 100)
+    Wf[3, :128] = np.float32(2.0 ** 120)
+    Wf[4] *= np.float32(2.0 ** 110)
+    Wf[4, 128:256] = np.float32(-(2.0 ** 120))
+    Wf[5, :256] *= np.float32(2.0 ** -125)            # one tiny group in an ordinary row
+    return Wf
+
+
+@pytest.mark.parametrize("fmt", [U8, HEAD])
+@pytest.mark.parametrize("K", [512, 1280])
+def test_scales_outside_the_reciprocal_range(torch, fmt, K):
+    Wf = extreme_weights(K, seed=37 + K)
+    want = oracle.quant_weight_i8(Wf, fmt)
+    if fmt == U8:
+        r = W.bf16_bits_to_f32(want[2]).astype(np.float64)
+        gs = want[1].astype(np.float64) * r[:, None]
+        small = r                                     # d = r * u8 with r subnormal
+    else:
+        gs = small = W.bf16_bits_to_f32(want[1]).astype(np.float64)
+    assert np.any((gs > 0) & (gs < 2.0 ** -120)) and np.any(gs > 2.0 ** 120)
+    assert np.any((small > 0) & (small < 2.0 ** -126))                    # subnormal scales
+    assert_same(run(torch, Wf, fmt), want)

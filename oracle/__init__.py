@@ -26,7 +26,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rad_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 builds and loads a copy instrumented with AddressSanitizer
+# and UndefinedBehaviorSanitizer (it aborts on the first finding).  The Python
+# process must then start with the ASan runtime preloaded:
+#   LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#   ORACLE_SANITIZE=1 python -m pytest tests -m "not gpu"
+SANITIZE = os.environ.get("ORACLE_SANITIZE", "") not in ("", "0")
+_LIB = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 FMT_U8G256_BF16ROW = 0
 FMT_BF16G128 = 1
@@ -42,11 +49,13 @@ _ERRORS = {
 
 
 def build(force: bool = True) -> str:
-    """Compile ``liboracle.so`` with gcc (-O2, no fast-math, no FP contraction)."""
+    """Compile ``liboracle.so`` with gcc (-O2, no fast-math, no FP contraction);
+    with ORACLE_SANITIZE set, the sanitizer-instrumented ``liboracle_san.so``."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-fPIC", "-shared", "-Wall", "-Wextra", *(_SAN_FLAGS if SANITIZE else []),
+               "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -12,20 +12,26 @@ is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
 activations and runs the int8 contraction and epilogue (for one token as a
 single fused kernel; otherwise the quantiser followed by the GEMV path for
 M <= 128 or the GEMM path above).  The default workload is the single-token
-decode of the fused gate_up projection (M=1, K=5120, N=34816).
+decode of the fused gate_up projection (M=1, K=5120, N=34816); the same run
+then measures the metric's other half, the 8K-token prefill through the down
+projection (M=8192, K=17408, N=5120), and reports it under "prefill_down"
+(--only skips it).
 
-The weights rotate over enough distinct copies (>= 1 GiB) that the 256 MiB
-last-level cache cannot serve a repeated read.  Steps are replayed from a HIP
-graph unless --eager is given: one graph holds one round of the copies for
-M > 128, and about 64 steps (several rounds) for M <= 128, as an engine
-captures a whole forward pass.
+Each workload runs `--warmup` untimed steps (the first one eager, before any
+graph capture), then exactly `--steps` timed steps between two HIP events on
+one stream.  The weights rotate over enough distinct copies (>= 1 GiB) that
+the 256 MiB last-level cache cannot serve a repeated read.  Steps are
+replayed from HIP graphs of up to 1000 steps unless --eager is given.
 
 One JSON line is printed.  `value` is the step's algorithmic bytes (f32
 activations in, weight codes and scales in, f32 outputs out, each counted
 once) per second for M <= 128, or 2*M*N*K int8 operations per second for
 larger M.  `roofline` is the dominant kernel timed alone with HIP events on
-its own stream, against MI355X's published peak.  `cpu_baseline` is the CPU
-oracle on a bounded sample of the same workload.
+its own stream, against MI355X's published peak; for the matrix-core kernel
+it also gives the core clock read with amdsmi while that kernel runs back to
+back (after the timed region) and the fraction of the peak at that clock.
+`cpu_baseline` is the CPU oracle on a bounded sample of the same workload,
+with the host's core count and CPU model.
 
 --op quant_weight times rad_quant_weight_i8 instead: quantising synthetic f32
 weights of the named workload's weight shape and format (one launch per
@@ -71,6 +77,11 @@ METRIC = "W8A8 rotated linear: HBM GB/s (M≤128) and int8 TOPS (M=8192), % of r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 COPY_TARGET_BYTES = 1 << 30    # distinct weight bytes rotated through per round
+PEAK_CLOCK_MHZ = 2400.0        # MI355X peak engine clock, at which the published peaks hold
+DEFAULT_WORKLOAD = "decode_gate_up"
+DEFAULT_STEPS = 200            # timed steps when --steps is not given
+DEFAULT_WARMUP = 20            # untimed steps before them when --warmup is not given
+MAX_GRAPH_STEPS = 1000         # calls per captured HIP graph
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed f32 lane-operations, 39.3 T/s
 WQ_CANDIDATES = 16             # scale candidates per group of rad_quant_weight_i8
 WQ_OPS_PER_EVAL = 8            # operations per (weight, candidate) evaluation
@@ -81,7 +92,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_gate_up")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="the layer's workload (default: the one-token decode, followed in the "
+                         "same run by the 8K-token prefill, the metric's two halves)")
+    ap.add_argument("--only", action="store_true",
+                    help="with the default workload, skip the prefill half")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip reading the core clock under the M > 128 kernel")
     ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore",
                                      "fwht", "quant_act"),
                     default="linear",
@@ -251,6 +268,76 @@ def traffic_from(args):
     print(json.dumps(rec))
 
 
+def cpu_model():
+    """The host CPU's model name (for the oracle baseline), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sustained_clock(fn, seconds=2.0, settle=0.75):
+    """Median GPU core clock (MHz) and socket power (W) read with amdsmi while
+    `fn` (a batch of launches of the dominant kernel) runs back to back for
+    about `seconds`, outside any timed region; readings from the first
+    `settle` seconds (while the power controller and the firmware's averages
+    catch up with the load) are dropped.  None where amdsmi or its readings
+    are unavailable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    clocks, power = [], []
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            if time.perf_counter() - t0 < settle:
+                time.sleep(0.005)
+                continue
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                c = m.get("current_gfxclk")
+                if isinstance(c, (int, float)) and 0 < c < 10000:
+                    clocks.append(float(c))
+                p = m.get("current_socket_power")
+                if isinstance(p, (int, float)) and 0 < p < 10000:
+                    power.append(float(p))
+            except Exception:
+                pass
+            time.sleep(0.005)
+
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    if not clocks:
+        return None
+    return {"gfx_clock_mhz": float(np.median(clocks)),
+            "gfx_clock_mhz_range": [float(min(clocks)), float(max(clocks))],
+            "socket_power_w": float(np.median(power)) if power else None,
+            "samples": len(clocks), "seconds": round(time.perf_counter() - t0, 2),
+            "settle_seconds": settle, "source": "amdsmi gpu metrics: current_gfxclk, current_socket_power"}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -281,15 +368,34 @@ def main():
         bench_quant_weight(args, wl)
         return
     if args.op in ("fwht", "quant_act"):
-        bench_act(args, W.WORKLOADS["prefill_down"] if args.workload == "decode_gate_up" else wl)
+        bench_act(args, W.WORKLOADS["prefill_down"] if args.workload == DEFAULT_WORKLOAD else wl)
         return
     if args.op == "rescore":
-        bench_rescore(args, W.WORKLOADS["vocab_head"] if args.workload == "decode_gate_up" else wl)
+        bench_rescore(args, W.WORKLOADS["vocab_head"] if args.workload == DEFAULT_WORKLOAD else wl)
         return
+    out = bench_linear(args, wl)
+    if args.workload == DEFAULT_WORKLOAD and not args.only:
+        # the metric's second half, timed in the same run with the same step
+        # and warm-up counts: int8 TOPS of the 8K-token prefill
+        pre = bench_linear(args, W.WORKLOADS["prefill_down"])
+        out["prefill_down"] = {k: pre[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step",
+                                                   "config", "roofline", "cpu_baseline",
+                                                   "parity_on_timed_buffers")}
+    print(json.dumps(out))
+
+
+def bench_linear(args, wl):
+    """The whole layer on one workload; returns its JSON record."""
+    import torch
+    from rotated_w8a8_int8_amd import binding as B
+    from rotated_w8a8_int8_amd import workloads as W
+
     sz = sizes(wl)
     big = wl.M > B.RAD_GEMV_MAX_M
-    steps = args.steps if args.steps is not None else (20 if big else 3000)
-    warmup = args.warmup if args.warmup is not None else (3 if big else 200)
+    steps = args.steps if args.steps is not None else DEFAULT_STEPS
+    warmup = args.warmup if args.warmup is not None else DEFAULT_WARMUP
+    if steps < 1:
+        raise SystemExit("--steps must be at least 1")
     dev = torch.device("cuda", 0)
 
     inp = W.make_workload(wl.name, seed=0)
@@ -314,60 +420,68 @@ def main():
     fused = wl.M == 1 and wl.K <= 20480                 # rad_w8a8_linear runs one kernel
 
     def step(i):
-        B.linear(x, weights[i], q=q, scale=s, y=ys[i])
+        B.linear(x, weights[i % ncopies], q=q, scale=s, y=ys[i % ncopies])
 
     def contraction_only(i):
-        contract(q, s, weights[i], y=ys[i])
+        contract(q, s, weights[i % ncopies], y=ys[i % ncopies])
 
     stream = torch.cuda.Stream(device=dev)             # default priority
     torch.cuda.synchronize()
 
-    # calls per graph: for the short M <= 128 steps, several rounds over the
-    # weight copies go into one graph (as an engine captures a whole forward
-    # pass), so the per-replay launch cost is not charged to a handful of steps
-    per_round = ncopies * (1 if big else max(1, -(-64 // ncopies)))
-
-    def make_round(fn):
-        """One round = per_round calls, cycling over the weight copies;
-        graph-captured unless --eager."""
+    def runner(fn, n):
+        """A callable that enqueues exactly n calls fn(0), fn(1), ... (cycling
+        over the weight copies) on `stream`: HIP graphs of at most
+        MAX_GRAPH_STEPS calls each, or eager launches with --eager."""
+        if n <= 0:
+            return lambda: None
         if args.eager:
-            def run():
-                for i in range(per_round):
-                    fn(i % ncopies)
-            return run
-        with torch.cuda.stream(stream):
-            for i in range(ncopies):                   # warm the code path before capture
-                fn(i)
+            def run_eager():
+                for i in range(n):
+                    fn(i)
+            return run_eager
+        counts = [MAX_GRAPH_STEPS] * (n // MAX_GRAPH_STEPS)
+        if n % MAX_GRAPH_STEPS:
+            counts.append(n % MAX_GRAPH_STEPS)
+        graphs = {}
+        for m in sorted(set(counts)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(m):
+                    fn(i)
+            graphs[m] = g
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(per_round):
-                fn(i % ncopies)
-        torch.cuda.synchronize()
-        return g.replay
+        seq = [graphs[m] for m in counts]
+
+        def run_graphs():
+            for g in seq:
+                g.replay()
+        return run_graphs
 
     def timed(fn, n_calls, n_warm):
-        run = make_round(fn)
-        rounds = max(1, -(-n_calls // per_round))
-        wrounds = max(1, -(-n_warm // per_round)) if n_warm > 0 else 0
+        """max(n_warm, 1) untimed calls (the first one eager, before any graph
+        capture: it loads the kernels), then exactly n_calls calls timed with
+        HIP events on `stream`.  Returns (ms per call, host ms per call,
+        warm-up calls run, the timed callable)."""
         with torch.cuda.stream(stream):
-            for _ in range(wrounds):
-                run()
+            fn(0)
+        torch.cuda.synchronize()
+        warm = runner(fn, n_warm - 1)
+        run = runner(fn, n_calls)
+        with torch.cuda.stream(stream):
+            warm()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
             e0.record(stream)
-            for _ in range(rounds):
-                run()
+            run()
             e1.record(stream)
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-        ms = e0.elapsed_time(e1)
-        return ms / (rounds * per_round), (t1 - t0) * 1e3 / (rounds * per_round), rounds * per_round
+        return e0.elapsed_time(e1) / n_calls, (t1 - t0) * 1e3 / n_calls, max(n_warm, 1), run
 
-    # ---- the whole step
-    ms_step, wall_ms_step, nsteps = timed(step, steps, warmup)
+    # ---- the whole step: `warmup` untimed steps, then exactly `steps` timed ones
+    ms_step, wall_ms_step, warm_run, run_steps = timed(step, steps, warmup)
     if big:
         value = sz["ops"] / (ms_step * 1e-3) / 1e12
         unit = "TOPS"
@@ -379,9 +493,10 @@ def main():
     # One token: the step is a single fused kernel, so it is its own dominant
     # kernel and moves the step's bytes plus the codes and scale it writes out.
     if fused:
-        ms_k, kbytes, kname = ms_step, sz["step"] + wl.M * wl.K + wl.M * 4, "rad_w8a8_linear (fused)"
+        ms_k, run_k = ms_step, run_steps
+        kbytes, kname = sz["step"] + wl.M * wl.K + wl.M * 4, "rad_w8a8_linear (fused)"
     else:
-        ms_k, _, _ = timed(contraction_only, steps, warmup)
+        ms_k, _, _, run_k = timed(contraction_only, steps, warmup)
         kbytes, kname = sz["contraction"], ("rad_w8a8_gemm" if big else "rad_w8a8_gemv")
     if big:
         achieved = sz["ops"] / (ms_k * 1e-3) / 1e12
@@ -395,6 +510,20 @@ def main():
     roof["bytes_per_launch"] = kbytes
     roof["us_per_launch"] = round(ms_k * 1e3, 3)
     roof["traffic"] = load_traffic(wl)
+    if big and not args.no_clock:
+        # the matrix cores' peak scales with the core clock, which dense int8
+        # work on random codes holds below its 2.4 GHz maximum (power): read
+        # the clock while the same kernel runs back to back, outside the
+        # timed region, and state the peak and fraction at that clock
+        def again():
+            with torch.cuda.stream(stream):
+                run_k()
+        clk = sustained_clock(again)
+        if clk is not None:
+            roof["clock"] = clk
+            roof["peak_at_clock"] = round(INT8_PEAK_TOPS * clk["gfx_clock_mhz"] / PEAK_CLOCK_MHZ, 1)
+            roof["frac_at_clock"] = round(achieved / roof["peak_at_clock"], 4)
+
 
     # ---- context: the vendor's int8 GEMM on the same codes (same stream,
     # same weight copies, same launch mode).  It computes less than the
@@ -408,9 +537,9 @@ def main():
             outs = [torch.empty((wl.M, wl.N), dtype=torch.int32, device=dev) for _ in range(ncopies)]
 
             def vendor_call(i):
-                torch._int_mm(q, weights[i].codes.t(), out=outs[i])
+                torch._int_mm(q, weights[i % ncopies].codes.t(), out=outs[i % ncopies])
 
-            ms_v, _, _ = timed(vendor_call, steps, warmup)
+            ms_v, _, _, _ = timed(vendor_call, steps, warmup)
             vendor = {"library": "hipBLASLt via torch._int_mm",
                       "computes": "int32 codes x codes^T over all of K; no group or row scales, "
                                   "int32 output",
@@ -456,6 +585,7 @@ def main():
         else:
             cv = (sz["step"] - (wl.M - cpu_rows) * (wl.K * 4 + wl.N * 4)) / dt / 1e9
         cpu = {"value": round(cv, 4), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": "%d of %d tokens, whole weight, %d repetitions, %.1f s"
                          % (cpu_rows, wl.M, n, dt * n)}
 
@@ -464,8 +594,8 @@ def main():
         "value": round(value, 3),
         "unit": unit,
         "n_gpus": 1,
-        "steps": nsteps,
-        "warmup": warmup,
+        "steps": steps,
+        "warmup": warm_run,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -475,7 +605,7 @@ def main():
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
                    "format": {0: "u8g256_bf16row", 1: "bf16g128", 2: "tbl4_bf16g128"}[wl.fmt],
                    "weight_copies": ncopies, "launch": "eager" if args.eager else "hip_graph",
-                   "steps_per_launch": 1 if args.eager else per_round,
+                   "steps_per_launch": 1 if args.eager else min(steps, MAX_GRAPH_STEPS),
                    "host_ms_per_step": round(wall_ms_step, 5)},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -483,7 +613,8 @@ def main():
     }
     if vendor is not None:
         out["vendor_int8_gemm"] = vendor
-    print(json.dumps(out))
+    return out
+
 
 
 def bench_quant_weight(args, wl):

@@ -89,6 +89,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
+    const int wu = __builtin_amdgcn_readfirstlane(wid);  // the same, known uniform
     const int l16 = lane & 15;
     const int r4 = lane >> 4;                          // weight row inside the quad
     const int wave = blockIdx.x * 4 + wid;
@@ -103,6 +104,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
 
     // 1. this wave's group and row scales, straight into LDS, dword by dword.
     //    A dword that would run past the end of an array is loaded bytewise.
+    //    The direct loads are issued from asm (dma4): the compiler's wait
+    //    counting does not see them, so it does not drain them (nor the weight
+    //    loads behind them) before the rotation; they are older than every
+    //    load the compiler waits for, and the explicit full wait before the
+    //    weight stream covers them.
     {
         const uint8_t *gs = static_cast<const uint8_t *>(gscale);
         const int nd = cnt * qsb / 4;
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
             const int64_t src = static_cast<int64_t>(4 * (wave + qi * W)) * G * ESZ + (4 * j - qi * qsb);
             const bool ok = j < nd;
             if (ok && src + 4 <= allsb) {
-                g2lds_dword(gs + src, &sc_lds[wid][4 * j0]);
+                dma4(gs, static_cast<uint32_t>(src), lds_offset(&sc_lds[wu][4 * j0]));
             } else if (ok && src < allsb) {
                 for (int b = 0; b < 4 && src + b < allsb; ++b) sc_lds[wid][4 * j + b] = gs[src + b];
             }
@@ -124,14 +130,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
             const int64_t src = static_cast<int64_t>(8) * (wave + qi * W) + 4 * (j & 1);
             const bool ok = j < 2 * cnt;
             if (ok && src + 4 <= 2 * static_cast<int64_t>(N)) {
-                g2lds_dword(rs + src, &rs_lds[wid][0]);
+                dma4(rs, static_cast<uint32_t>(src), lds_offset(&rs_lds[wu][0]));
             } else if (ok && src < 2 * static_cast<int64_t>(N)) {
                 for (int b = 0; b < 4 && src + b < 2 * static_cast<int64_t>(N); ++b) rs_lds[wid][4 * j + b] = rs[src + b];
             }
         }
     }
 
-    // 2. the token: f32 into registers (fused) or its codes straight into LDS
+    // 2. the token: f32 into registers (fused) or its codes straight into LDS.
+    //    The fused loads are branch-free (blocks past the row re-read the last
+    //    block and are zeroed after the load): with no branch around them the
+    //    compiler's wait before the rotation counts only the weight loads
+    //    issued after them, so the rotation runs while those are in flight.
     Blk8 xv[FUSED ? NQ : 1];
     float s = 0.0f;
     const int nblk = K >> 7;
@@ -139,14 +149,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
 #pragma unroll
         for (int it = 0; it < NQ; ++it) {
             const int blk = (it * 4 + wid) * 4 + r4;
-            if (blk < nblk) {
-                const float *p = x + blk * 128 + 4 * l16;
-                xv[it].lo = *reinterpret_cast<const float4 *>(p);
-                xv[it].hi = *reinterpret_cast<const float4 *>(p + 64);
-            } else {
-                xv[it].lo = make_float4(0.f, 0.f, 0.f, 0.f);
-                xv[it].hi = xv[it].lo;
-            }
+            const float *p = x + min(blk, nblk - 1) * 128 + 4 * l16;
+            xv[it].lo = *reinterpret_cast<const float4 *>(p);
+            xv[it].hi = *reinterpret_cast<const float4 *>(p + 64);
         }
     } else {
         for (int d0 = wid * 64; d0 < K / 4; d0 += 256) {
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
     //    exactly ceil(K / 256), so only the last step can hold lanes past the
     //    end of a row (head format), and those are clamped and not accumulated.
     auto row_ptr = [&](int i) -> const int8_t * {
-        const int ii = min(i, cnt - 1);
+        const int ii = max(min(i, cnt - 1), 0);
         const int row = min(4 * (wave + ii * W) + r4, N - 1);
         return codes + static_cast<int64_t>(row) * RB + 16 * l16;
     };
@@ -174,33 +179,49 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
         }
         return ld16(rp + 256 * t);
     };
+    // (a wave without quads loads a clamped row, never used).  The
+    // scheduling fences keep all D loads after the token's and ahead of the
+    // rotation, which then waits for the token only.
     v4i ring[D];
     const int8_t *rp_next = row_ptr(0);
-    if (cnt > 0) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < D; ++t) ring[t] = wload(rp_next, t);
-    }
+    for (int t = 0; t < D; ++t) ring[t] = wload(rp_next, t);
+    __builtin_amdgcn_sched_barrier(0);
 
     // 4. fused: rotate and quantise the token into LDS (and, block 0, to q / s)
     if constexpr (FUSED) {
         float amax = 0.0f;
 #pragma unroll
         for (int it = 0; it < NQ; ++it) {
-            fwht128_regs(xv[it], l16);
+            if ((it * 4 + wid) * 4 + r4 >= nblk) {
+                xv[it].lo = make_float4(0.f, 0.f, 0.f, 0.f);
+                xv[it].hi = xv[it].lo;
+            }
+            fwht128_regs_signed(xv[it], l16);   // values times the lane sign c
             amax = fmaxf(amax, fmaxf(amax4(xv[it].lo), amax4(xv[it].hi)));
         }
         amax = wave_max_f32(amax);
         if (lane == 0) red[wid] = amax;
         __syncthreads();
         s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / 127.0f;
+        // codes through the reciprocal where that provably rounds like the
+        // division (the same scheme and bits as rad_quant_act_i8), else
+        // through the division
+        const bool fast = s >= 0x1p-120f;
+        const float c = fwht_lane_sign(l16);
+        const float rs_c = c * (1.0f / s);
 #pragma unroll
         for (int it = 0; it < NQ; ++it) {
             const int blk = (it * 4 + wid) * 4 + r4;
             if (blk < nblk) {
                 uint32_t lo = 0, hi = 0;
-                if (s != 0.0f) {
-                    lo = pack4(xv[it].lo, s);
-                    hi = pack4(xv[it].hi, s);
+                if (fast) {
+                    lo = pack4_rcp_signed(xv[it].lo, s, rs_c, c);
+                    hi = pack4_rcp_signed(xv[it].hi, s, rs_c, c);
+                } else if (s != 0.0f) {
+                    lo = pack4_signed(xv[it].lo, s, c);
+                    hi = pack4_signed(xv[it].hi, s, c);
                 }
                 const int off = blk * 128 + 4 * l16;
                 *reinterpret_cast<uint32_t *>(&q_lds[off]) = lo;
@@ -247,7 +268,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
                     p = dot16_i8(ring[t % D], av, 0);
                 }
                 if constexpr (FMT == kFmtU8) {
-                    const int prod = p * static_cast<int>(scq[t]);     // |prod| < 2^26
+                    // |p| <= 16 * 127^2 < 2^23: a full-rate 24-bit multiply
+                    const int prod = __mul24(p, static_cast<int>(scq[t]));     // |prod| < 2^26
                     if constexpr (STEPS <= 32) {
                         acc += prod;                                   // < 32 * 2^26
                     } else {
@@ -679,6 +701,10 @@ inline bool m1_supported(int64_t K, int fmt) {
 
 hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st) {
+    if (M == 1 && decode_row_supported(w)) {
+        return launch_decode_row(nullptr, const_cast<int8_t *>(q), const_cast<float *>(s), w, y, partials,
+                                 false, st);                     // read only: not fused
+    }
     if (M == 1 && m1_supported(w.K, w.fmt)) {
         int8_t *qi = const_cast<int8_t *>(q);            // read only: FUSED == false
         float *si = const_cast<float *>(s);
@@ -691,10 +717,13 @@ hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, flo
     return launch_skinny<kFmtTbl4>(q, s, w, y, M, partials, st);
 }
 
-bool fused_decode_supported(const WeightArgs &w, int64_t M) { return M == 1 && m1_supported(w.K, w.fmt); }
+bool fused_decode_supported(const WeightArgs &w, int64_t M) {
+    return M == 1 && (decode_row_supported(w) || m1_supported(w.K, w.fmt));
+}
 
 hipError_t launch_fused_decode(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
                                hipStream_t st) {
+    if (decode_row_supported(w)) return launch_decode_row(x, q, s, w, y, nullptr, true, st);
     if (w.fmt == kFmtU8) return launch_m1<kFmtU8, true>(x, q, s, w, y, nullptr, st);
     if (w.fmt == kFmtHead) return launch_m1<kFmtHead, true>(x, q, s, w, y, nullptr, st);
     return launch_m1<kFmtTbl4, true>(x, q, s, w, y, nullptr, st);

@@ -81,11 +81,12 @@ __global__ __launch_bounds__(WAVES * 64) void quant_act_kernel(const float *__re
             v[it].hi = v[it].lo;
         }
     }
+    if (rotate) {
 #pragma unroll
-    for (int it = 0; it < NITER; ++it) {
-        if (rotate) fwht128_regs(v[it], l16);
-        amax = fmaxf(amax, fmaxf(amax4(v[it].lo), amax4(v[it].hi)));
+        for (int it = 0; it < NITER; ++it) fwht128_regs_signed(v[it], l16);   // values times the lane sign c
     }
+#pragma unroll
+    for (int it = 0; it < NITER; ++it) amax = fmaxf(amax, fmaxf(amax4(v[it].lo), amax4(v[it].hi)));
     amax = wave_max_f32(amax);
     if (lane == 0) red[wid] = amax;
     __syncthreads();
@@ -100,7 +101,8 @@ __global__ __launch_bounds__(WAVES * 64) void quant_act_kernel(const float *__re
     // for a finite reciprocal use the division throughout (s is per token,
     // so the branch is uniform)
     const bool fast = s >= 0x1p-120f;
-    const float rs = 1.0f / s;
+    const float c = rotate ? fwht_lane_sign(l16) : 1.0f;
+    const float rs_c = c * (1.0f / s);
     int8_t *qr = q + m * K;
 #pragma unroll
     for (int it = 0; it < NITER; ++it) {
@@ -108,11 +110,11 @@ __global__ __launch_bounds__(WAVES * 64) void quant_act_kernel(const float *__re
         if (blk < nblk) {
             uint32_t lo = 0, hi = 0;
             if (fast) {
-                lo = pack4_rcp(v[it].lo, s, rs);
-                hi = pack4_rcp(v[it].hi, s, rs);
+                lo = pack4_rcp_signed(v[it].lo, s, rs_c, c);
+                hi = pack4_rcp_signed(v[it].hi, s, rs_c, c);
             } else if (s != 0.0f) {
-                lo = pack4(v[it].lo, s);
-                hi = pack4(v[it].hi, s);
+                lo = pack4_signed(v[it].lo, s, c);
+                hi = pack4_signed(v[it].hi, s, c);
             }
             int8_t *p = qr + blk * 128 + 4 * l16;
             *reinterpret_cast<uint32_t *>(p) = lo;

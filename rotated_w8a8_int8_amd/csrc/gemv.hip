@@ -619,21 +619,6 @@ __global__ __launch_bounds__(64 * (kSkMaxW + 1)) void skinny_kernel(const int8_t
         }
 }
 
-// Compute units of the current device, looked up once per device.
-int device_cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 // Compute waves per workgroup.  A workgroup costs its rows plus a fixed part
 // that does not shrink with them (its own pass of the M x K activation codes
 // through LDS, the pipeline fill and drain), and a CU runs one wide
@@ -665,7 +650,7 @@ int sk_compute_waves(int64_t N, int cus) {
 template <int FMT, int MB>
 hipError_t launch_skinny_t(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                            int32_t *P, hipStream_t st) {
-    const int cus = device_cu_count();
+    const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int nw = sk_compute_waves(w.N, cus);
     const int64_t rows_per_wg = 16 * static_cast<int64_t>(nw);
@@ -698,6 +683,20 @@ inline bool m1_supported(int64_t K, int fmt) {
 }
 
 }  // namespace
+
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                        int32_t *partials, hipStream_t st) {

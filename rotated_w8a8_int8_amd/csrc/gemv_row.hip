@@ -26,9 +26,7 @@
 // FUSED: the workgroup first rotates and quantises the f32 token (the same
 // device code, bits and reciprocal scheme as rad_quant_act_i8) while its first
 // weight loads are in flight; block 0 also writes the codes and the scale.
-// Only four waves of a workgroup stream weights (more streams at once measured
-// slower); a fused workgroup has twelve more that share the rotation, so it
-// takes one pass instead of three, and then end.
+// (Workgroups with extra waves that only share the rotation measured slower.)
 #include "rad_device.h"
 #include "rad_launch.h"
 #include "rotate_quant.h"
@@ -57,11 +55,10 @@ __device__ __forceinline__ int64_t wave_sum_exact(int v) {
     return h * 65536 + l;
 }
 
-constexpr int kRowStreamWaves = 4;              // weight-streaming waves of a workgroup
-template <bool FUSED> constexpr int kRowWgWaves = FUSED ? 4 : kRowStreamWaves;
+constexpr int kRowWgWaves = 4;                   // waves of a workgroup
 
 template <int NS, bool FUSED, bool WRITE_P>
-__global__ __launch_bounds__(64 * kRowWgWaves<FUSED>) void decode_row_kernel(const float *__restrict__ x,
+__global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_kernel(const float *__restrict__ x,
                                                          int8_t *__restrict__ qio,
                                                          float *__restrict__ sio,
                                                          const int8_t *__restrict__ codes,
@@ -73,17 +70,16 @@ __global__ __launch_bounds__(64 * kRowWgWaves<FUSED>) void decode_row_kernel(con
     constexpr int R = RowShape<NS>::R, D = RowShape<NS>::D;
     constexpr int G = K / 256;                     // groups of a row; its scales are NS dwords
     constexpr int NBLK = K / 128;
-    constexpr int WGW = kRowWgWaves<FUSED>;        // waves of a workgroup
+    constexpr int WGW = kRowWgWaves;
     constexpr int NQ = (NBLK + 4 * WGW - 1) / (4 * WGW);   // rotation steps: 4 blocks a wave
     __shared__ __attribute__((aligned(16))) int8_t q_lds[FUSED ? K : 16];
     __shared__ float red[WGW];
 
     const int lane = threadIdx.x & 63;
     const int wid = threadIdx.x >> 6;
-    const bool streams = wid < kRowStreamWaves;    // wave-uniform
     const int l16 = lane & 15, r4 = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kRowStreamWaves + wid);
-    const int W = gridDim.x * kRowStreamWaves;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * WGW + wid);
+    const int W = gridDim.x * WGW;
     const int cnt = wave < N ? (N - wave + W - 1) / W : 0;   // rows of this wave
     const int groups = (cnt + R - 1) / R;
     // row j of this wave, clamped in bounds (loads past the wave's last row
@@ -114,18 +110,10 @@ __global__ __launch_bounds__(64 * kRowWgWaves<FUSED>) void decode_row_kernel(con
 
     // 2. the first D weight loads (rows 0 .. R-1), kept behind the token's
     //    loads and ahead of the rotation, which then waits for the token only
-    //    (rotation-only waves load the token's first bytes instead, cache
-    //    hits, so that every wave's wait counts stay the same, branch-free)
     v4i ring[D];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-        if constexpr (FUSED)
-            ring[i] = streams ? wload(i / NS, i % NS)
-                              : ld16_nt(reinterpret_cast<const int8_t *>(x) + 1024 * (i % NS) + 16 * lane);
-        else
-            ring[i] = wload(i / NS, i % NS);
-    }
+    for (int i = 0; i < D; ++i) ring[i] = wload(i / NS, i % NS);
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. fused: rotate and quantise the token into LDS (block 0: to q and s)
@@ -173,7 +161,6 @@ __global__ __launch_bounds__(64 * kRowWgWaves<FUSED>) void decode_row_kernel(con
         }
         if (blockIdx.x == 0 && threadIdx.x == 0) sio[0] = s;
         __syncthreads();
-        if (!streams) return;
 #pragma unroll
         for (int t = 0; t < NS; ++t) a[t] = *reinterpret_cast<const v4i *>(&q_lds[1024 * t + 16 * lane]);
     }
@@ -222,21 +209,24 @@ __global__ __launch_bounds__(64 * kRowWgWaves<FUSED>) void decode_row_kernel(con
     }
 }
 
-// Waves in all: about kRowWaves, rounded so that every wave's row count is a
-// whole number of rings where possible.
-constexpr int kRowWaves = 1024;
-
+// One workgroup of four waves per CU: measured on MI355X (decode_gate_up,
+// 256 CUs), 1024 waves in all streamed fastest; more waves (two workgroups on
+// some or all CUs), fewer (idle CUs), deeper rings and a deeper first ring
+// were all slower.  Rows per wave are rounded to whole rings where possible.
 template <int NS, bool FUSED>
 hipError_t launch_row_t(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y, int32_t *P,
                         hipStream_t st) {
     constexpr int R = RowShape<NS>::R;
     const int N = static_cast<int>(w.N);
-    int per = (N + kRowWaves - 1) / kRowWaves;              // rows per wave
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const int target = kRowWgWaves * cus;
+    int per = (N + target - 1) / target;                    // rows per wave
     per = ((per + R - 1) / R) * R;
     const int waves = (N + per - 1) / per;
-    const int grid = (waves + kRowStreamWaves - 1) / kRowStreamWaves;
+    const int grid = (waves + kRowWgWaves - 1) / kRowWgWaves;
     auto kern = P ? decode_row_kernel<NS, FUSED, true> : decode_row_kernel<NS, FUSED, false>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kRowWgWaves<FUSED>), 0, st, x, q, s, w.codes,
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kRowWgWaves), 0, st, x, q, s, w.codes,
                        static_cast<const uint32_t *>(w.gscale), w.rscale, y, P, N);
     return hipGetLastError();
 }

@@ -16,6 +16,9 @@ struct WeightArgs {
     int fmt;                 // 0: u8 per 256 + bf16 row; 1: bf16 per 128; 2: codebook, bf16 per 128
 };
 
+// Compute units of the current device (looked up once per device), or 0.
+int cu_count();
+
 hipError_t launch_fwht128(const float *x, float *y, int64_t rows, int64_t K, hipStream_t st);
 hipError_t launch_quant_act(const float *x, int8_t *q, float *s, int64_t M, int64_t K, int rotate,
                             hipStream_t st);

@@ -33,7 +33,6 @@
 // conflicts (rocprofv3 SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.50 on
 // both the 128-token trunk and the 64-token head); r & 15 took the 128-token
 // trunk shape from 50.3 to 47.9 us and left the head unchanged.
-#include <atomic>
 
 #include "rad_device.h"
 #include "rad_launch.h"
@@ -433,21 +432,6 @@ hipError_t launch_t(const int8_t *q, const float *s, const WeightArgs &w, float 
     return hipGetLastError();
 }
 
-// Compute units of the current device, looked up once per device.
-int lds_cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    if (dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 }  // namespace
 
 // A CU holds one of these workgroups at a time (LDS), so the kernel takes
@@ -463,7 +447,7 @@ int lds_cu_count() {
 bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
     if (w.fmt == 2) {
         if (M < 9 || M > 16 || w.K % (2 * kSlKC) != 0) return false;
-        const int cus = lds_cu_count();
+        const int cus = cu_count();
         if (cus <= 0) return false;
         const int64_t wgs = (w.N + ShapeT16::BN - 1) / ShapeT16::BN;
         const int64_t rounds = (wgs + cus - 1) / cus;
@@ -479,7 +463,7 @@ bool skinny_lds_supported(const WeightArgs &w, int64_t M) {
     if (M >= 33 && M <= 64) bn = w.fmt == kFmtU8 ? Shape64::BN : ShapeH64::BN;
     else if (M >= 112 && M <= 128) bn = Shape128::BN;
     else return false;
-    const int cus = lds_cu_count();
+    const int cus = cu_count();
     if (cus <= 0) return false;
     const int64_t wgs = (w.N + bn - 1) / bn;
     const int64_t rounds = (wgs + cus - 1) / cus;

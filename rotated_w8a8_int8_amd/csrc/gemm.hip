@@ -24,6 +24,10 @@
 // handed a slab of 4 M-tiles x all N-tiles, walked M-fastest, so the ~32
 // workgroups an XCD runs at once share their activation rows and weight
 // columns in that XCD's L2.
+//
+// On random codes the chip runs this kernel at its power limit (1400 W, the
+// core clock well below its 2.4 GHz maximum), so the time per call follows
+// the energy spent per operation rather than the issue schedule alone.
 #include <type_traits>
 
 #include "rad_device.h"
@@ -58,6 +62,7 @@ __device__ __forceinline__ void tile_of(int b, int tiles_m, int tiles_n, int &tm
 
 constexpr int kStages = 3;
 constexpr int kABytes = kBM * kKC, kBBytes = kBN * kKC;   // one stage of each operand
+constexpr int kStageBytes = kABytes + kBBytes;            // a stage: A rows, then B rows
 constexpr int kDmaA = kABytes / 1024 / kWaves;            // 1 KiB loads per wave per stage
 constexpr int kDmaB = kBBytes / 1024 / kWaves;
 constexpr int kDmaPerStage = kDmaA + kDmaB;
@@ -71,6 +76,12 @@ constexpr int kDmaPerStage = kDmaA + kDmaB;
 // different 16-byte slots of a 128-byte bank line, and any 16 hit all 16
 // slots of a 256-byte line (rows of equal parity differ in the swizzle).
 __device__ __forceinline__ int lds_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// 16-byte LDS read at a byte address.
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+__device__ __forceinline__ v4i lds_ld16(uint32_t addr) {
+    return *reinterpret_cast<lds_v4i *>(addr);
+}
 __device__ __forceinline__ int lds_chunk_addr(int row, int c) {
     return 128 * row + 16 * (c ^ lds_swz(row));
 }
@@ -86,8 +97,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
                                                         int K, int tiles_m, int tiles_n) {
     constexpr int GW = (FMT == kFmtU8) ? 256 : 128;
     constexpr int SPG = GW / kKC;                      // stages per group
-    __shared__ __attribute__((aligned(1024))) int8_t As[kStages][kABytes];
-    __shared__ __attribute__((aligned(1024))) int8_t Bs[kStages][kBBytes];
+    // one allocation, so every fragment address is a uniform stage base plus
+    // one per-lane offset (one VALU op per read)
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageBytes];
     // per group: each wave's 64 columns, one dword each (the dword that holds
     // the column's scale), filled by direct loads like the operands
     __shared__ __attribute__((aligned(256))) uint32_t Ss[kStages][kWaves][kWTN];
@@ -134,10 +146,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
         const int buf = ks % kStages;
         if (j < kDmaA)
             dma16(abase + static_cast<int64_t>(kc) * kKC, aoffs[j],
-                  lds_offset(&As[buf][(wu * kDmaA + j) * 1024]));
+                  lds_offset(&smem[buf * kStageBytes + (wu * kDmaA + j) * 1024]));
         else
             dma16(bbase + static_cast<int64_t>(kc) * kKC, boffs[j - kDmaA],
-                  lds_offset(&Bs[buf][(wu * kDmaB + j - kDmaA) * 1024]));
+                  lds_offset(&smem[buf * kStageBytes + kABytes + (wu * kDmaB + j - kDmaA) * 1024]));
     };
     auto issue_stage = [&](int ks) {
 #pragma unroll
@@ -212,14 +224,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
     };
 
     // LDS byte offsets of this lane's fragments at k-step 0 of a stage: rows
-    // of the wave's 32 x 32 tiles, chunk lq.  K-step kk reads chunk
-    // 2 kk + lq, i.e. the k-step 0 offset XOR 32 kk (the swizzle is an XOR
-    // on the chunk index and 2 kk, lq occupy disjoint bits).
+    // of the wave's 32 x 32 tiles, chunk 4 lq.  K-step kk reads chunk
+    // kk + 4 lq, i.e. the k-step 0 offset XOR 16 kk (the swizzle is an XOR
+    // on the chunk index and kk, 4 lq occupy disjoint bits); A and B use the
+    // same assignment, so each matrix op sums 32 K positions of its stage.
+    // 16 kk is an inline constant, so each read's address is one
+    // xor-and-add of the lane offset with the uniform stage base.
     int aoff[kTM], boff[kTN];
 #pragma unroll
-    for (int t = 0; t < kTM; ++t) aoff[t] = lds_chunk_addr(wm * kWTM + t * 32 + li, lq);
+    for (int t = 0; t < kTM; ++t) aoff[t] = lds_chunk_addr(wm * kWTM + t * 32 + li, 4 * lq);
 #pragma unroll
-    for (int t = 0; t < kTN; ++t) boff[t] = lds_chunk_addr(wn * kWTN + t * 32 + li, lq);
+    for (int t = 0; t < kTN; ++t) boff[t] = lds_chunk_addr(wn * kWTN + t * 32 + li, 4 * lq);
 
     // Issue order (every vector-memory operation of the loop is a direct LDS
     // load issued from asm, so the only waits are the explicit ones below):
@@ -260,8 +275,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
             if constexpr (SPG == 1) issue_scales(min(g + 1, G - 1));
             else if (st == 0) issue_scales(g);
             if (st == 0 && g > 0) read_scales(g - 1, scf);
-            const int8_t *Ab = As[ks % kStages];
-            const int8_t *Bb = Bs[ks % kStages];
+            // uniform stage bases, opaque to the compiler so that it keeps
+            // them in scalar registers instead of moving constants into the
+            // per-lane address arithmetic
+            uint32_t sa = lds_offset(&smem[(ks % kStages) * kStageBytes]);
+            uint32_t sb = sa + kABytes;
+            asm volatile("" : "+s"(sa), "+s"(sb));
             // opaque per stage: keeps the per-k-step XORs below in the loop
             // instead of 16 hoisted, always-live address registers
 #pragma unroll
@@ -273,9 +292,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
             v4i fa[2][kTM], fb[2][kTN];
             auto read_frags = [&](int kk, v4i(&a)[kTM], v4i(&b)[kTN]) {
 #pragma unroll
-                for (int t = 0; t < kTM; ++t) a[t] = *reinterpret_cast<const v4i *>(Ab + (aoff[t] ^ (32 * kk)));
+                for (int t = 0; t < kTM; ++t) a[t] = lds_ld16(sa + (aoff[t] ^ (16 * kk)));
 #pragma unroll
-                for (int t = 0; t < kTN; ++t) b[t] = *reinterpret_cast<const v4i *>(Bb + (boff[t] ^ (32 * kk)));
+                for (int t = 0; t < kTN; ++t) b[t] = lds_ld16(sb + (boff[t] ^ (16 * kk)));
             };
             read_frags(0, fa[0], fb[0]);
 #pragma unroll

@@ -99,6 +99,11 @@ def parse():
                     help="with the default workload, skip the prefill half")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip reading the core clock under the M > 128 kernel")
+    ap.add_argument("--codes", choices=("random", "constant", "zero"), default="random",
+                    help="int8 formats: replace the synthetic codes by constant ones (one nonzero "
+                         "per 128-block of x, so every rotated activation code is 127, and weight "
+                         "codes of 127) or by zeros, to see how the codes' switching moves the "
+                         "power and clock (the default is the workload's random codes)")
     ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore",
                                      "fwht", "quant_act"),
                     default="linear",
@@ -401,6 +406,15 @@ def bench_linear(args, wl):
     dev = torch.device("cuda", 0)
 
     inp = W.make_workload(wl.name, seed=0)
+    if args.codes != "random":
+        if wl.fmt == W.FMT_TBL4_BF16G128:
+            raise SystemExit("--codes applies to the int8 formats")
+        inp.x[:] = 0.0
+        if args.codes == "constant":
+            inp.x[:, ::128] = 1.0
+            inp.qw[:] = 127
+        else:
+            inp.qw[:] = 0
 
     def to_dev(a):
         a = np.ascontiguousarray(a)
@@ -541,13 +555,18 @@ def bench_linear(args, wl):
             def vendor_call(i):
                 torch._int_mm(q, weights[i % ncopies].codes.t(), out=outs[i % ncopies])
 
-            ms_v, _, _, _ = timed(vendor_call, steps, warmup)
+            ms_v, _, _, run_v = timed(vendor_call, steps, warmup)
             vendor = {"library": "hipBLASLt via torch._int_mm",
                       "computes": "int32 codes x codes^T over all of K; no group or row scales, "
                                   "int32 output",
                       "us_per_launch": round(ms_v * 1e3, 3),
                       "tops": round(sz["ops"] / (ms_v * 1e-3) / 1e12, 2),
                       "rad_over_vendor_time": round(ms_k / ms_v, 4)}
+            if big and not args.no_clock:
+                def again_v():
+                    with torch.cuda.stream(stream):
+                        run_v()
+                vendor["clock"] = sustained_clock(again_v)
             # cross-check on four tokens: the library's exact group partials,
             # summed over the groups, are the vendor's int32 products
             _, P4 = B.w8a8_gemv(q[:4], s[:4], weights[0], partials=True)
@@ -604,7 +623,7 @@ def bench_linear(args, wl):
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N,
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "codes": args.codes,
                    "format": {0: "u8g256_bf16row", 1: "bf16g128", 2: "tbl4_bf16g128"}[wl.fmt],
                    "weight_copies": ncopies, "launch": "eager" if args.eager else "hip_graph",
                    "steps_per_launch": 1 if args.eager else min(steps, MAX_GRAPH_STEPS),

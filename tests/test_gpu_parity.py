@@ -201,6 +201,53 @@ def test_gemv_m1_u8_output_is_exact(torch):
     assert np.array_equal(y.view(np.int32), yr.view(np.int32))
 
 
+# One token in the trunk format with K a multiple of 1024 streams whole weight
+# rows, 1 KiB of a row per load instruction, with a ring of rows per wave whose
+# depth depends on K / 1024: every supported K, a row count below the number
+# of waves, a ragged one, and (short K) many ring turns per wave; codes given
+# (rad_w8a8_gemv) and fused (rad_w8a8_linear).
+ROW_STEPS = [1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 17, 20]
+
+
+@pytest.mark.parametrize("steps", ROW_STEPS)
+def test_one_token_whole_row_kernel(torch, steps):
+    K = 1024 * steps
+    for N in (7, 2500 + 37 * steps) + ((40000,) if steps <= 2 else ()):
+        print("K", K, "N", N, flush=True)
+        inp = W.make(1, K, N, 0, seed=100 * steps + N)
+        q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+        assert np.array_equal(P, oracle.group_partials(q, inp.qw, 0))
+        yr = oracle.linear(q, s, inp.qw, 0, inp.gscale, inp.rscale)
+        assert np.array_equal(y.view(np.int32), yr.view(np.int32))
+        y2, _ = B.w8a8_gemv(qd, sd, w)
+        assert np.array_equal(host(y2).view(np.int32), yr.view(np.int32))
+        yf, qf, sf = B.linear(dev(torch, inp.x), w)
+        assert np.array_equal(host(sf).view(np.int32), s.view(np.int32))
+        assert np.array_equal(host(qf), q)
+        assert np.array_equal(host(yf).view(np.int32), yr.view(np.int32))
+
+
+def test_one_token_whole_row_extreme_sums(torch):
+    # the largest per-lane sums the kernel can meet: K = 20480, every
+    # activation code 127 (one equal nonzero per 128-block rotates to a
+    # constant block), weight codes +-127 and every group scale 255
+    K, N = 20480, 300
+    inp = W.make(1, K, N, 0, seed=9)
+    x = np.zeros((1, K), np.float32)
+    x[0, ::128] = np.float32(1.5)
+    qw = np.where((np.arange(N) % 2 == 0)[:, None], np.int8(127), np.int8(-127)) * np.ones((1, K), np.int8)
+    gscale = np.full_like(inp.gscale, 255)
+    inp = W.Inputs(x, np.ascontiguousarray(qw.astype(np.int8)), gscale, inp.rscale, 0)
+    q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+    assert np.all(q == 127)
+    assert np.array_equal(P, oracle.group_partials(q, inp.qw, 0))
+    yr = oracle.linear(q, s, inp.qw, 0, inp.gscale, inp.rscale)
+    assert np.array_equal(y.view(np.int32), yr.view(np.int32))
+    yf, qf, sf = B.linear(dev(torch, x), w)
+    assert np.array_equal(host(qf), q)
+    assert np.array_equal(host(yf).view(np.int32), yr.view(np.int32))
+
+
 GEMM_SMALL = [
     (1, 256, 16, 0), (5, 512, 256, 0), (130, 512, 130, 0), (257, 768, 300, 1), (128, 1024, 128, 0),
     (200, 256, 33, 0), (300, 640, 70, 1), (129, 2048, 257, 0),

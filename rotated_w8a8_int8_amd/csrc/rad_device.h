@@ -28,8 +28,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 
 // ---- DPP lane exchanges inside one 16-lane row --------------------------
 // Each returns the value held by lane (lane ^ X) of the same row.  xor 1 and
-// xor 2 are single quad permutations; xor 4 and xor 8 compose a mirror with a
-// second permutation (half-mirror maps i -> i^7, mirror maps i -> i^15).
+// xor 2 are single quad permutations, xor 8 is the row rotation by 8 (i ->
+// (i + 8) mod 16 = i ^ 8); xor 4 composes the half-row mirror (i -> i ^ 7)
+// with quad permutation [3,2,1,0].
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
@@ -37,13 +38,13 @@ __device__ __forceinline__ int dpp(int v) {
 constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kQuadXor3 = 0x1B;        // quad_perm [3,2,1,0]
-constexpr int kRowMirror = 0x140;      // lane i <- 15 - i
+constexpr int kRowRor8 = 0x128;        // lane i <- (i + 8) mod 16 = i ^ 8
 constexpr int kRowHalfMirror = 0x141;  // lane i <- i ^ 7
 
 __device__ __forceinline__ int lane_xor1(int v) { return dpp<kQuadXor1>(v); }
 __device__ __forceinline__ int lane_xor2(int v) { return dpp<kQuadXor2>(v); }
 __device__ __forceinline__ int lane_xor4(int v) { return dpp<kQuadXor3>(dpp<kRowHalfMirror>(v)); }
-__device__ __forceinline__ int lane_xor8(int v) { return dpp<kRowHalfMirror>(dpp<kRowMirror>(v)); }
+__device__ __forceinline__ int lane_xor8(int v) { return dpp<kRowRor8>(v); }
 
 template <int X>
 __device__ __forceinline__ int lane_xor(int v) {

@@ -68,10 +68,9 @@ __device__ __forceinline__ void bfly_x4(float4 &v, bool upper) {
 
 // The four cross-lane stages on a lane's eight values, as one block of DPP
 // fused multiply-adds (v_fmac_f32 with its first source read from the partner
-// lane): partner l ^ 1 and l ^ 2 are single quad permutations; l ^ 4 is the
-// half-row mirror (l -> l ^ 7) followed by quad permutation [3,2,1,0], l ^ 8
-// the row mirror (l -> l ^ 15) followed by the half-row mirror, the first
-// permutation staged in a temporary with a DPP move.  Written as one asm block
+// lane): partner l ^ 1 and l ^ 2 are single quad permutations, l ^ 8 the row
+// rotation by 8; l ^ 4 is the half-row mirror (l -> l ^ 7), staged in a
+// temporary with a DPP move, followed by quad permutation [3,2,1,0].  Written as one asm block
 // because the compiler does not fold its DPP moves into v_fmac_f32.  Hazards:
 // a DPP read of a VGPR needs two wait states after the VALU write of it; the
 // leading s_nop 1 covers the writes before the block, and inside it every
@@ -111,8 +110,7 @@ __device__ __forceinline__ void fwht_cross_lane(Blk8 &b, float m1, float m2, flo
         RAD_FMAC8("quad_perm:[2,3,0,1]", "%17")
         RAD_MOV8("row_half_mirror")
         RAD_FMACT8("quad_perm:[3,2,1,0]", "%18")
-        RAD_MOV8("row_mirror")
-        RAD_FMACT8("row_half_mirror", "%19")
+        RAD_FMAC8("row_ror:8", "%19")
         : "+v"(b.lo.x), "+v"(b.lo.y), "+v"(b.lo.z), "+v"(b.lo.w),
           "+v"(b.hi.x), "+v"(b.hi.y), "+v"(b.hi.z), "+v"(b.hi.w),
           "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
@@ -183,11 +181,11 @@ __device__ __forceinline__ uint32_t pack4(float4 v, float s) {
 // The same codes through the reciprocal: t = v * fl(1/s) lies within
 // 1.5 * 2^-23 |v / s| (< 2^-15 here, |v / s| <= 127.06) of the rounded
 // quotient fl(v / s), so both round to the same integer unless t is within
-// 2^-13 of a half-integer (about 1 element in 4000).  pack4_rcp codes four
-// elements that way and, if any lane of the wave holds such an element among
-// its four, redoes the four with the IEEE division in a wave-uniform branch
-// (taken for about 6% of the four-element groups of a wave).  Needs s in
-// [2^-120, 2^120] (1/s finite and normal).
+// 2^-13 of a half-integer (about 1 element in 4000).  pack4_rcp_signed codes
+// four elements that way and, if any lane of the wave holds such an element
+// among its four, redoes the four with the IEEE division in a wave-uniform
+// branch (taken for about 6% of the four-element groups of a wave).  Needs s
+// in [2^-120, 2^120] (1/s finite and normal).
 __device__ __forceinline__ float quant1_rcp(float v, float rs, bool &near) {
     const float t = v * rs;
     const float r = __builtin_rintf(t);
@@ -198,26 +196,12 @@ __device__ __forceinline__ float quant1_rcp(float v, float rs, bool &near) {
     return r;
 }
 
-__device__ __forceinline__ uint32_t pack4_rcp(float4 v, float s, float rs) {
-    bool near = false;
-    float r0 = quant1_rcp(v.x, rs, near), r1 = quant1_rcp(v.y, rs, near);
-    float r2 = quant1_rcp(v.z, rs, near), r3 = quant1_rcp(v.w, rs, near);
-    if (__any(near)) {
-        r0 = __builtin_rintf(v.x / s);
-        r1 = __builtin_rintf(v.y / s);
-        r2 = __builtin_rintf(v.z / s);
-        r3 = __builtin_rintf(v.w / s);
-    }
-    auto byte = [](float r) {
-        return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f))) & 0xFFu;
-    };
-    return byte(r0) | (byte(r1) << 8) | (byte(r2) << 16) | (byte(r3) << 24);
-}
-
 // Codes of c * v (c = +-1, the lane sign of fwht128_regs_signed) for a
-// lane holding v: the reciprocal scheme of pack4_rcp with rs_c = c * fl(1/s)
-// (so v * rs_c equals (c v) * fl(1/s) bit for bit, the sign aside rounding
-// alike), and the division fallback on c * v, formed exactly.
+// lane holding v: the reciprocal scheme above with rs_c = c * fl(1/s) (so
+// v * rs_c equals (c v) * fl(1/s) bit for bit, the sign aside rounding
+// alike), and the division fallback on c * v, formed exactly.  No clamp: with
+// s = fl(amax / 127) normal and |v| <= amax, |v / s| and |v * fl(1/s)| stay
+// below 127 (1 + 2^-21), so both round to at most 127 in magnitude.
 __device__ __forceinline__ uint32_t pack4_rcp_signed(float4 v, float s, float rs_c, float c) {
     bool near = false;
     float r0 = quant1_rcp(v.x, rs_c, near), r1 = quant1_rcp(v.y, rs_c, near);
@@ -228,9 +212,7 @@ __device__ __forceinline__ uint32_t pack4_rcp_signed(float4 v, float s, float rs
         r2 = __builtin_rintf((c * v.z) / s);
         r3 = __builtin_rintf((c * v.w) / s);
     }
-    auto byte = [](float r) {
-        return static_cast<uint32_t>(static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f))) & 0xFFu;
-    };
+    auto byte = [](float r) { return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu; };
     return byte(r0) | (byte(r1) << 8) | (byte(r2) << 16) | (byte(r3) << 24);
 }
 __device__ __forceinline__ uint32_t pack4_signed(float4 v, float s, float c) {

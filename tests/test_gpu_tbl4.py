@@ -57,6 +57,32 @@ def test_tbl4_layer_partials_and_outputs(torch, M, K, N):
     rows_close(y.cpu().numpy(), oracle.epilogue(Pr, s, TBL, inp.gscale, None))
 
 
+# One token with K a multiple of 1024 up to 8192 streams two weight rows per
+# load instruction (512 bytes each): every such K, an odd row count (a last
+# pair with one row), fewer pairs than waves, and several ring turns a wave;
+# codes given (partials too) and fused.
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 8])
+def test_tbl4_one_token_whole_row(torch, steps):
+    K = 1024 * steps
+    for N in (7, 3001 + 2 * steps) + ((20001,) if steps <= 2 else ()):
+        print("K", K, "N", N, flush=True)
+        inp = W.make(1, K, N, TBL, seed=7 * steps + N)
+        q, s = oracle.quant_act_i8(inp.x)
+        w = weight(torch, inp)
+        qd, sd = dev(torch, q), dev(torch, s)
+        y, P = B.w8a8_gemv(qd, sd, w, partials=True)
+        Pr = oracle.group_partials(q, inp.qw, TBL)
+        assert np.array_equal(P.cpu().numpy(), Pr)
+        yr = oracle.epilogue(Pr, s, TBL, inp.gscale, None)
+        rows_close(y.cpu().numpy(), yr)
+        y2, _ = B.w8a8_gemv(qd, sd, w)
+        assert np.array_equal(y2.cpu().numpy(), y.cpu().numpy())
+        yf, qf, sf = B.linear(dev(torch, inp.x), w)
+        assert np.array_equal(qf.cpu().numpy(), q)
+        assert np.array_equal(sf.cpu().numpy().view(np.int32), s.view(np.int32))
+        assert np.array_equal(yf.cpu().numpy(), y.cpu().numpy())
+
+
 # 9..16 tokens on enough weight rows (144-row workgroups filling >= 85% of a
 # round on a 256-CU MI355X) take the kernel that stages both operands through
 # LDS: ragged last workgroups, one and many stages of K, 9 and 16 tokens.

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
     __syncthreads();
 
     // 5. the weight stream
+    [[maybe_unused]] const Tbl4Masks tk = tbl4_masks();
     for (int i = 0; i < cnt; ++i) {
         const int row = 4 * (wave + i * W) + r4;
         const int8_t *rp_cur = rp_next;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const float *__restrict__ x
                 int p;
                 if constexpr (FMT == kFmtTbl4) {
                     v4i lo, hi;
-                    tbl4_decode16(ring[t % D], lo, hi);
+                    tbl4_decode16(ring[t % D], lo, hi, tk);
                     const v4i a0 = *reinterpret_cast<const v4i *>(&q_lds[32 * c + qoff]);
                     const v4i a1 = *reinterpret_cast<const v4i *>(&q_lds[32 * c + 16 + qoff]);
                     p = dot16_i8(hi, a1, dot16_i8(lo, a0, 0));
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(64 * (kSkMaxW + 1)) void skinny_kernel(const int8_t
         return 128 * row + 16 * (c ^ sk_swz(row));
     };
 
+    [[maybe_unused]] const Tbl4Masks tk = tbl4_masks();
     // one stage: s the stage, i = s mod kSkD its ring slot (a constant after
     // unrolling)
     auto stage = [&](int s, int i) {
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(64 * (kSkMaxW + 1)) void skinny_kernel(const int8_t
         const int8_t *Ab = As[s % kSkRing];
         v4i bw[2];                                    // the stage's B operands
         if constexpr (FMT == kFmtTbl4) {
-            tbl4_decode16(wr[i][0], bw[0], bw[1]);
+            tbl4_decode16(wr[i][0], bw[0], bw[1], tk);
         } else {
             bw[0] = wr[i][0];
             bw[1] = wr[i][1];

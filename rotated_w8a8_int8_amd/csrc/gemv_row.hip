@@ -311,6 +311,7 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_tbl4_kernel(const
         }
     }
 
+    const Tbl4Masks tk = tbl4_masks();
     const int sperm = 4 * (32 * h + l32 / 8);      // byte address of this lane's scale lane at t = 0
     const int shift = 16 * ((l32 >> 2) & 1);
     auto sload = [&](int j) -> uint32_t {
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_tbl4_kernel(const
             for (int t = 0; t < NS; ++t) {
                 const int i = rr * NS + t;
                 v4i lo, hi;
-                tbl4_decode16(ring[i], lo, hi);
+                tbl4_decode16(ring[i], lo, hi, tk);
                 const int p = dot16_i8(hi, a1[t], dot16_i8(lo, a0[t], 0));
                 const uint32_t sd = static_cast<uint32_t>(
                     __builtin_amdgcn_ds_bpermute(sperm + 16 * t, static_cast<int>(scr[rr])));

@@ -158,6 +158,19 @@ constexpr uint32_t kTbl4_1 = tbl4_dword(-43, -30, -18, -6);
 constexpr uint32_t kTbl4_2 = tbl4_dword(6, 18, 30, 43);
 constexpr uint32_t kTbl4_3 = tbl4_dword(58, 75, 97, 127);
 
+// The three byte masks of the lookups below, held in VGPRs for a whole
+// kernel (create them once, outside its loops): with them in registers each
+// pick selector is one v_and_or_b32, a three-operand instruction that takes no
+// literal on this chip, instead of an and, an or and their literals.
+struct Tbl4Masks {
+    uint32_t m7, m4, base;
+};
+__device__ __forceinline__ Tbl4Masks tbl4_masks() {
+    Tbl4Masks k{0x07070707u, 0x04040404u, 0x03020100u};
+    asm volatile("" : "+v"(k.m7), "+v"(k.m4), "+v"(k.base));
+    return k;
+}
+
 // One 16-byte run of packed indices (32 elements: byte b holds element b in
 // its low nibble and element 16 + b in its high nibble) -> the int8 values of
 // elements 0..15 (lo) and 16..31 (hi).  Per dword of indices: v_perm looks up
@@ -169,12 +182,12 @@ __device__ __forceinline__ uint32_t tbl4_lookup4(uint32_t sel7, uint32_t pick) {
     const uint32_t hi = __builtin_amdgcn_perm(kTbl4_3, kTbl4_2, sel7);   // entries 8..15
     return __builtin_amdgcn_perm(hi, lo, pick);
 }
-__device__ __forceinline__ void tbl4_decode16(v4i packed, v4i &lo, v4i &hi) {
+__device__ __forceinline__ void tbl4_decode16(v4i packed, v4i &lo, v4i &hi, const Tbl4Masks &k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w = static_cast<uint32_t>(packed[i]);
-        lo[i] = static_cast<int>(tbl4_lookup4(w & 0x07070707u, ((w >> 1) & 0x04040404u) | 0x03020100u));
-        hi[i] = static_cast<int>(tbl4_lookup4((w >> 4) & 0x07070707u, ((w >> 5) & 0x04040404u) | 0x03020100u));
+        lo[i] = static_cast<int>(tbl4_lookup4(w & k.m7, ((w >> 1) & k.m4) | k.base));
+        hi[i] = static_cast<int>(tbl4_lookup4((w >> 4) & k.m7, ((w >> 5) & k.m4) | k.base));
     }
 }
 

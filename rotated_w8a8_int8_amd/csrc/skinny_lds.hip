@@ -343,6 +343,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
     // weight run 4 p + q of row r sits at (256 r + 16 (q ^ (r & 7))) ^ 64 p
     const int boff = kSlKC * (16 * wid + j) + 16 * (qd ^ (j & 7));
 
+    const Tbl4Masks tk = tbl4_masks();
 #pragma unroll
     for (int p = 0; p < NST - 1; ++p) issue_stage(p);
     for (int s = 0; s < NS; ++s) {
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             v4i lo, hi;
-            tbl4_decode16(*reinterpret_cast<const v4i *>(Bb + (boff ^ (64 * p))), lo, hi);
+            tbl4_decode16(*reinterpret_cast<const v4i *>(Bb + (boff ^ (64 * p))), lo, hi, tk);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 v4i a[MB];

@@ -80,7 +80,7 @@ COPY_TARGET_BYTES = 1 << 30    # distinct weight bytes rotated through per round
 PEAK_CLOCK_MHZ = 2400.0        # MI355X peak engine clock, at which the published peaks hold
 DEFAULT_WORKLOAD = "decode_gate_up"
 DEFAULT_STEPS = 200            # timed steps when --steps is not given
-DEFAULT_WARMUP = 20            # untimed steps before them when --warmup is not given
+DEFAULT_WARMUP = 200           # untimed steps before them when --warmup is not given
 MAX_GRAPH_STEPS = 1000         # calls per captured HIP graph
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12   # non-packed f32 lane-operations, 39.3 T/s
 WQ_CANDIDATES = 16             # scale candidates per group of rad_quant_weight_i8
@@ -832,7 +832,7 @@ def bench_act(args, wl):
     fwht = args.op == "fwht"
     M, K = wl.M, wl.K
     steps = args.steps if args.steps is not None else 100
-    warmup = args.warmup if args.warmup is not None else 10
+    warmup = args.warmup if args.warmup is not None else 200      # ~25 ms: memory clocks settle
     x = W.make_workload(wl.name).x
     dev = torch.device("cuda", 0)
     per = M * K * (8 if fwht else 5)
@@ -931,7 +931,7 @@ def bench_kv(args):
     rows, D = W.KV_WORKLOADS[name]
     enc = args.op == "kv_quant"
     steps = args.steps if args.steps is not None else 200
-    warmup = args.warmup if args.warmup is not None else 20
+    warmup = args.warmup if args.warmup is not None else 200
     x = W.make_kv(rows, D, seed=0)
     dev = torch.device("cuda", 0)
     # enough distinct copies that the 256 MiB last-level cache cannot serve repeats

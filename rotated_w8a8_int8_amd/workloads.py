@@ -83,6 +83,12 @@ WORKLOADS = {
                  "drafter linear on the 4-bit codebook, one token"),
         Workload("drafter_block", 16, 5120, 34816, FMT_TBL4_BF16G128,
                  "drafter linear on the 4-bit codebook, 16-token draft block"),
+        # one GPU's share of the two headline workloads split eight ways:
+        # decode over N (columns), prefill over M (tokens)
+        Workload("decode_gate_up_n8", 1, 5120, 4352, FMT_U8G256_BF16ROW,
+                 "one GPU's column share (N / 8) of decode_gate_up"),
+        Workload("prefill_down_m8", 1024, 17408, 5120, FMT_U8G256_BF16ROW,
+                 "one GPU's token share (M / 8) of prefill_down"),
     )
 }
 ORDER = ["tiny", "decode_gate_up", "verify_skinny", "prefill_down", "vocab_head"]

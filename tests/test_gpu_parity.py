@@ -338,7 +338,7 @@ def test_linear_zero_token(torch):
 
 @pytest.mark.parametrize("name,fn", [
     ("tiny", "gemv"), ("decode_gate_up", "gemv"), ("verify_skinny", "gemv"), ("vocab_head", "gemv"),
-    ("tiny", "gemm"),
+    ("tiny", "gemm"), ("decode_gate_up_n8", "gemv"),
 ])
 def test_workload_full_size(torch, name, fn):
     """Every token row of the workload: codes, scales, all group partials and
@@ -365,13 +365,14 @@ def test_workload_full_size(torch, name, fn):
     assert np.array_equal(host(y2).view(np.int32), y.view(np.int32))
 
 
-def test_prefill_full_size_every_row(torch):
-    """prefill_down (8192 x 17408 x 5120) on the GEMM: every code and scale,
-    then all 8192 x 5120 x 68 group partials and every output, compared in
-    chunks of 512 token rows against the oracle."""
-    wl = W.WORKLOADS["prefill_down"]
-    print("workload prefill_down gemm, every row", flush=True)
-    inp = W.make_workload("prefill_down", seed=0)
+@pytest.mark.parametrize("name", ["prefill_down", "prefill_down_m8"])
+def test_prefill_full_size_every_row(torch, name):
+    """prefill_down (8192 x 17408 x 5120) and one GPU's 1024-token share of
+    it on the GEMM: every code and scale, then all group partials and every
+    output, compared in chunks of 512 token rows against the oracle."""
+    wl = W.WORKLOADS[name]
+    print("workload", name, "gemm, every row", flush=True)
+    inp = W.make_workload(name, seed=0)
     xd = dev(torch, inp.x)
     qd, sd = B.quant_act_i8(xd)
     q, s = oracle.quant_act_i8(inp.x)

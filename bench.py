@@ -67,6 +67,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -186,11 +187,21 @@ def kernel_sources(wl):
     return ["gemm.hip"] + common
 
 
+def code_text(src):
+    """Source text without comments and blank lines, so that a comment edit
+    does not count as a kernel change."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+
+
 def kernel_source_hash(wl):
+    """sha256[:16] of the code (comments stripped) of the dominant kernel's sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rotated_w8a8_int8_amd", "csrc")
     for f in sorted(kernel_sources(wl)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,6 @@
-// gemv_row.hip -- the trunk layer for one token (M == 1) with weight rows
-// streamed whole, 1 KiB per load instruction (gfx950).
+// gemv_row.hip -- the layer for one token (M == 1) with weight rows streamed
+// whole, 1 KiB per load instruction: the trunk's int8 format, and below it
+// the drafter's 4-bit codebook format (gfx950).
 //
 // What is computed (model card "Qwen3.8-27B IQ8R + DFlash2 -- radiance
 // container", table rows "Weights" and "Activations"): int8 activation codes

@@ -68,3 +68,34 @@ def test_product_package_never_imports_the_oracle():
             for line in open(os.path.join(dirpath, f)):
                 if line.lstrip().startswith("#include"):
                     assert "oracle" not in line, (f, line)
+
+
+def test_traffic_records_are_keyed_on_their_kernels_code():
+    # every stored HBM traffic record names the dominant kernel's sources and
+    # a hash of their code (comments stripped); bench.py reports the record
+    # only while that hash matches the sources, and null after a kernel change
+    sys.path.insert(0, ROOT)
+    import json
+    import bench
+    from rotated_w8a8_int8_amd import workloads as W
+    assert bench.code_text("a // x\n/* y\n z */ b\n\n  c  \n") == "a\n b\n  c"
+    for name in ("decode_gate_up", "verify_skinny", "vocab_head", "prefill_down", "drafter_decode",
+                 "drafter_block"):
+        wl = W.WORKLOADS[name]
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % name)))
+        assert rec["kernel_sources"] == bench.kernel_sources(wl)
+        same = rec["kernel_source_sha256_16"] == bench.kernel_source_hash(wl)
+        assert bench.load_traffic(wl) == (rec["bytes_per_launch"] if same else None)
+        assert 1.0 <= rec["traffic_over_algorithmic"] < 4.5
+
+
+def test_one_token_kernel_sources_follow_the_launch_rules():
+    sys.path.insert(0, ROOT)
+    import bench
+    from rotated_w8a8_int8_amd import workloads as W
+    row = ["gemv_row.hip", "rotate_quant.h", "rad_device.h", "rad_launch.h"]
+    assert bench.kernel_sources(W.WORKLOADS["decode_gate_up"]) == row
+    assert bench.kernel_sources(W.WORKLOADS["drafter_decode"]) == row
+    assert bench.kernel_sources(W.Workload("x", 1, 640, 10, W.FMT_BF16G128, ""))[0] == "gemv.hip"
+    assert bench.kernel_sources(W.Workload("x", 1, 10240, 10, W.FMT_TBL4_BF16G128, ""))[0] == "gemv.hip"
+    assert bench.kernel_sources(W.WORKLOADS["prefill_down"])[0] == "gemm.hip"

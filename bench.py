@@ -176,7 +176,8 @@ def lds_kernel_applies(wl, cus=256):
 def kernel_sources(wl):
     """The source files the dominant kernel of a workload's step is built from."""
     common = ["rad_device.h", "rad_launch.h"]
-    if wl.M == 1 and wl.K % 1024 == 0 and (wl.fmt == 0 or (wl.fmt == 2 and wl.K <= 8192)):
+    if wl.M == 1 and wl.K % 1024 == 0 and (wl.fmt == 0 or (wl.fmt == 1 and wl.K <= 16384)
+                                           or (wl.fmt == 2 and wl.K <= 8192)):
         return ["gemv_row.hip", "rotate_quant.h"] + common   # whole-row one-token kernels
     if wl.M == 1:
         return ["gemv.hip", "rotate_quant.h"] + common       # the fused one-token kernel

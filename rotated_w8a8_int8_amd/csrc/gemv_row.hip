@@ -29,6 +29,9 @@
 // weight loads are in flight; block 0 also writes the codes and the scale.
 // (Workgroups with extra waves that only share the rotation measured slower.)
 //
+// The head format (bf16 scale per 128 of K) uses the same layout with an f32
+// fold of the group scales.
+//
 // The drafter's codebook format (model card, table row "Speculator": 4-bit
 // indices into a 16-level table, bf16 scale per 128) has a variant below:
 // a row is K / 2 bytes, so one load instruction reads 512 bytes of each of
@@ -235,6 +238,103 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_kernel(const floa
     }
 }
 
+// The head format (int8 codes, a bf16 scale per 128 of K), K a multiple of
+// 1024 up to 16384: the layout, ring and prologue of the kernel above.  Lane l
+// meets group 8 t + l / 8 at step t; a row's K / 128 bf16 scales are K / 256
+// dwords, loaded one per lane with the row (lanes past them re-load the
+// last), and at step t a lane fetches dword 4 t + l / 16 with a lane permute
+// and takes its half (l / 8) % 2.  Each lane folds its 16-element dot product
+// times the group scale into an f32 sum; the wave adds the 64 sums in a fixed
+// order, and y = s * 2^-7 * sum.
+template <int NS, bool FUSED, bool WRITE_P>
+__global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_head_kernel(const float *__restrict__ x,
+                                                              int8_t *__restrict__ qio,
+                                                              float *__restrict__ sio,
+                                                              const int8_t *__restrict__ codes,
+                                                              const uint32_t *__restrict__ gscale,
+                                                              float *__restrict__ y,
+                                                              int32_t *__restrict__ partials, int N) {
+    constexpr int K = NS * 1024;
+    constexpr int R = RowShape<NS>::R, D = RowShape<NS>::D;
+    constexpr int G = K / 128;                     // groups of a row: G / 2 scale dwords
+    constexpr int SD = G / 2;
+    static_assert(SD <= 64, "one scale dword of the row per lane");
+    constexpr int NBLK = K / 128;
+    constexpr int WGW = kRowWgWaves;
+    constexpr int NQ = (NBLK + 4 * WGW - 1) / (4 * WGW);
+    __shared__ __attribute__((aligned(16))) int8_t q_lds[FUSED ? K : 16];
+    __shared__ float red[WGW];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = threadIdx.x >> 6;
+    const int l16 = lane & 15, r4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * WGW + wid);
+    const int W = gridDim.x * WGW;
+    const int cnt = wave < N ? (N - wave + W - 1) / W : 0;   // rows of this wave
+    const int groups = (cnt + R - 1) / R;
+    auto row_of = [&](int j) { return min(wave + min(j, max(cnt - 1, 0)) * W, N - 1); };
+    auto wload = [&](int j, int t) -> v4i {
+        return ld16_nt(codes + static_cast<int64_t>(row_of(j)) * K + 1024 * t + 16 * lane);
+    };
+
+    Blk8 xv[NQ];
+    v4i a[NS];
+    float s = 0.0f;
+    if constexpr (FUSED) {
+        token_load<NQ, NBLK, WGW>(x, xv, wid, r4, l16);
+    } else {
+#pragma unroll
+        for (int t = 0; t < NS; ++t) a[t] = ld16(qio + 1024 * t + 16 * lane);
+        s = sio[0];
+    }
+
+    v4i ring[D];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) ring[i] = wload(i / NS, i % NS);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (FUSED) {
+        s = token_quantise<NQ, NBLK, WGW>(xv, q_lds, red, qio, sio, wid, r4, l16, lane);
+#pragma unroll
+        for (int t = 0; t < NS; ++t) a[t] = *reinterpret_cast<const v4i *>(&q_lds[1024 * t + 16 * lane]);
+    }
+
+    const int sperm = 4 * (lane / 16);             // byte address of this lane's scale lane at t = 0
+    const int shift = 16 * ((lane >> 3) & 1);
+    auto sload = [&](int j) -> uint32_t {
+        return gscale[static_cast<int64_t>(row_of(j)) * SD + min(lane, SD - 1)];
+    };
+    uint32_t scr[R];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) scr[rr] = sload(rr);
+    const float sy = s * 0x1p-7f;
+    for (int gi = 0; gi < groups; ++gi) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int j = gi * R + rr;
+            const int row = row_of(j);
+            float accf = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+                const int i = rr * NS + t;
+                const int p = dot16_i8(ring[i], a[t], 0);
+                const uint32_t sd = static_cast<uint32_t>(
+                    __builtin_amdgcn_ds_bpermute(sperm + 16 * t, static_cast<int>(scr[rr])));
+                accf += static_cast<float>(p) * bf16_to_f32(static_cast<uint16_t>((sd >> shift) & 0xFFFFu));
+                if constexpr (WRITE_P) {
+                    const int pg = row8_sum(p);
+                    if ((lane & 7) == 0 && j < cnt) partials[static_cast<int64_t>(row) * G + 8 * t + lane / 8] = pg;
+                }
+                ring[i] = wload(j + R, t);
+            }
+            scr[rr] = sload(j + R);
+            const float tot = wave_sum_f32(accf);
+            if (lane == 0 && j < cnt) y[row] = sy * tot;
+        }
+    }
+}
+
 // The codebook format, K a multiple of 1024 up to 8192.  Wave w owns row
 // pairs w, w + W, ...; lanes 0..31 stream the pair's first row and lanes
 // 32..63 its second, 512 bytes of packed indices a row per load instruction,
@@ -389,6 +489,15 @@ hipError_t launch_row_t(const float *x, int8_t *q, float *s, const WeightArgs &w
     const int waves = (units + per - 1) / per;
     const int grid = (waves + kRowWgWaves - 1) / kRowWgWaves;
     const uint32_t *gs = static_cast<const uint32_t *>(w.gscale);
+    if (w.fmt == 1) {
+        if constexpr (NS <= 16) {
+            auto kern = P ? decode_row_head_kernel<NS, FUSED, true> : decode_row_head_kernel<NS, FUSED, false>;
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kRowWgWaves), 0, st, x, q, s, w.codes, gs, y, P, N);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;                      // excluded by decode_row_supported
+        }
+    }
     if (tbl) {
         if constexpr (NS <= 8) {
             auto kern = P ? decode_row_tbl4_kernel<NS, FUSED, true> : decode_row_tbl4_kernel<NS, FUSED, false>;
@@ -423,7 +532,8 @@ bool decode_row_supported(const WeightArgs &w) {
     if (w.K % 1024 != 0) return false;
     const int64_t ns = w.K / 1024;
     if (w.fmt == 2) return ns <= 6 || ns == 8;               // codebook: K <= 8192
-    if (w.fmt != 0) return false;
+    if (w.fmt == 1 && ns > 16) return false;                  // head: K <= 16384
+    if (w.fmt != 0 && w.fmt != 1) return false;
     switch (ns) {
         case 1: case 2: case 3: case 4: case 5: case 6: case 8: case 10: case 12: case 16: case 17: case 20:
             return true;

@@ -30,10 +30,10 @@ hipError_t launch_gemv(const int8_t *q, const float *s, const WeightArgs &w, flo
 bool skinny_lds_supported(const WeightArgs &w, int64_t M);
 hipError_t launch_skinny_lds(const int8_t *q, const float *s, const WeightArgs &w, float *y, int64_t M,
                              int32_t *partials, hipStream_t st);
-// One token, K a multiple of 1024: the u8 format up to K = 20480 (weight rows
-// streamed whole, 1 KiB per load) and the codebook format up to K = 8192 (two
-// rows per load, 512 bytes each); optionally fused with the rotation and
-// quantisation of the token.
+// One token, K a multiple of 1024: the u8 format up to K = 20480 and the head
+// format up to K = 16384 (weight rows streamed whole, 1 KiB per load), the
+// codebook format up to K = 8192 (two rows per load, 512 bytes each);
+// optionally fused with the rotation and quantisation of the token.
 bool decode_row_supported(const WeightArgs &w);
 hipError_t launch_decode_row(const float *x, int8_t *q, float *s, const WeightArgs &w, float *y,
                              int32_t *partials, bool fused, hipStream_t st);

@@ -83,6 +83,8 @@ WORKLOADS = {
                  "drafter linear on the 4-bit codebook, one token"),
         Workload("drafter_block", 16, 5120, 34816, FMT_TBL4_BF16G128,
                  "drafter linear on the 4-bit codebook, 16-token draft block"),
+        Workload("head_decode", 1, 5120, 152064, FMT_BF16G128,
+                 "vocabulary head for one decoded token"),
         # one GPU's share of the two headline workloads split eight ways:
         # decode over N (columns), prefill over M (tokens)
         Workload("decode_gate_up_n8", 1, 5120, 4352, FMT_U8G256_BF16ROW,

@@ -3,8 +3,8 @@ that way): each call is run eagerly, then captured once and replayed several
 times with other eager library work and synchronisations between the
 replays; the outputs are poisoned before every replay and must come back
 bit-equal to the eager results each time.  Shapes cover every contraction
-kernel: the whole-row and quad one-token kernels, the register-streaming and
-LDS-staged M <= 128 kernels, the codebook kernels and the GEMM.
+kernel: the whole-row one-token kernels (each format) and the quad one, the
+register-streaming and LDS-staged M <= 128 kernels, and the GEMM.
 """
 import numpy as np
 import pytest
@@ -71,6 +71,7 @@ def replay_and_check(torch, capture, outputs, other):
 LINEAR = [
     (1, 5120, 3000, W.FMT_U8G256_BF16ROW),     # whole-row one-token kernel, fused
     (1, 640, 700, W.FMT_BF16G128),             # quad one-token kernel, fused
+    (1, 5120, 3000, W.FMT_BF16G128),           # whole-row one-token kernel, head format
     (1, 1024, 900, W.FMT_TBL4_BF16G128),       # codebook one-token kernel
     (16, 768, 2000, W.FMT_U8G256_BF16ROW),     # register-streaming M <= 128 kernel
     (128, 256, 33000, W.FMT_U8G256_BF16ROW),   # LDS-staged kernel

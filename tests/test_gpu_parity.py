@@ -227,6 +227,27 @@ def test_one_token_whole_row_kernel(torch, steps):
         assert np.array_equal(host(yf).view(np.int32), yr.view(np.int32))
 
 
+# The head format (bf16 scale per 128) with K a multiple of 1024 up to 16384
+# takes the same whole-row layout with an f32 fold: partials bit-exact,
+# outputs within the tolerance, fused equal to unfused.
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 8, 10, 12, 16])
+def test_one_token_whole_row_head_format(torch, steps):
+    K = 1024 * steps
+    for N in (7, 2500 + 37 * steps):
+        print("head K", K, "N", N, flush=True)
+        inp = W.make(1, K, N, 1, seed=300 * steps + N)
+        q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)
+        Pr = oracle.group_partials(q, inp.qw, 1)
+        assert np.array_equal(P, Pr)
+        assert_rows_close(y, oracle.epilogue(Pr, s, 1, inp.gscale, None))
+        y2, _ = B.w8a8_gemv(qd, sd, w)
+        assert np.array_equal(host(y2), y)
+        yf, qf, sf = B.linear(dev(torch, inp.x), w)
+        assert np.array_equal(host(sf).view(np.int32), s.view(np.int32))
+        assert np.array_equal(host(qf), q)
+        assert np.array_equal(host(yf), y)
+
+
 def test_one_token_whole_row_extreme_sums(torch):
     # the largest per-lane sums the kernel can meet: K = 20480, every
     # activation code 127 (one equal nonzero per 128-block rotates to a

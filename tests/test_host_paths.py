@@ -97,5 +97,7 @@ def test_one_token_kernel_sources_follow_the_launch_rules():
     assert bench.kernel_sources(W.WORKLOADS["decode_gate_up"]) == row
     assert bench.kernel_sources(W.WORKLOADS["drafter_decode"]) == row
     assert bench.kernel_sources(W.Workload("x", 1, 640, 10, W.FMT_BF16G128, ""))[0] == "gemv.hip"
+    assert bench.kernel_sources(W.WORKLOADS["head_decode"]) == row
+    assert bench.kernel_sources(W.Workload("x", 1, 17408, 10, W.FMT_BF16G128, ""))[0] == "gemv.hip"
     assert bench.kernel_sources(W.Workload("x", 1, 10240, 10, W.FMT_TBL4_BF16G128, ""))[0] == "gemv.hip"
     assert bench.kernel_sources(W.WORKLOADS["prefill_down"])[0] == "gemm.hip"

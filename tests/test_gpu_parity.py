@@ -359,7 +359,7 @@ def test_linear_zero_token(torch):
 
 @pytest.mark.parametrize("name,fn", [
     ("tiny", "gemv"), ("decode_gate_up", "gemv"), ("verify_skinny", "gemv"), ("vocab_head", "gemv"),
-    ("tiny", "gemm"), ("decode_gate_up_n8", "gemv"),
+    ("tiny", "gemm"), ("decode_gate_up_n8", "gemv"), ("head_decode", "gemv"),
 ])
 def test_workload_full_size(torch, name, fn):
     """Every token row of the workload: codes, scales, all group partials and

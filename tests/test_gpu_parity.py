@@ -181,7 +181,8 @@ def test_gemv_m_sweep(torch, M):
                                        (120, 512, 34000, 1), (112, 256, 31400, 0),
                                        (120, 1280, 31300, 0), (128, 768, 36000, 0),
                                        (64, 768, 46000, 1), (40, 2048, 53000, 1), (33, 256, 100000, 1),
-                                       (64, 256, 5, 0), (50, 384, 70, 1)])
+                                       (64, 256, 5, 0), (50, 384, 70, 1),
+                                       (112, 5120, 31400, 0), (120, 5120, 33000, 0), (128, 5120, 34810, 0)])
 def test_gemv_lds_path_shapes(torch, M, K, N, fmt):
     inp = W.make(M, K, N, fmt, seed=11 * M + K + N)
     q, s, y, P, (qd, sd, w) = run_linear(torch, B.w8a8_gemv, inp)

@@ -67,8 +67,7 @@ constexpr int kRowWgWaves = 4;                   // waves of a workgroup
 
 // The fused prologue, in two parts so the caller can issue its first weight
 // loads between them.  Each wave holds blocks (it * WGW + wid) * 4 + r4 of
-// the token, 16 lanes a block (blocks past the row re-read the last one and
-// are zeroed before the rotation).
+// the token, 16 lanes a block (blocks past the row re-read the last one).
 template <int NQ, int NBLK, int WGW>
 __device__ __forceinline__ void token_load(const float *__restrict__ x, Blk8 (&xv)[NQ], int wid, int r4,
                                            int l16) {
@@ -88,15 +87,17 @@ template <int NQ, int NBLK, int WGW>
 __device__ __forceinline__ float token_quantise(Blk8 (&xv)[NQ], int8_t *q_lds, float *red,
                                                 int8_t *__restrict__ qio, float *__restrict__ sio, int wid,
                                                 int r4, int l16, int lane) {
+    // A block past the row holds a re-read of the last one: it is rotated
+    // with the others and left out of the amax (its codes are never stored).
+    // Zeroing it before the rotation instead let the compiler make its load
+    // conditional and move it behind the first weight loads, so the rotation
+    // waited for all of them.
     float amax = 0.0f;
 #pragma unroll
     for (int it = 0; it < NQ; ++it) {
-        if ((it * WGW + wid) * 4 + r4 >= NBLK) {
-            xv[it].lo = make_float4(0.f, 0.f, 0.f, 0.f);
-            xv[it].hi = xv[it].lo;
-        }
         fwht128_regs_signed(xv[it], l16);   // values times the lane sign c
-        amax = fmaxf(amax, fmaxf(amax4(xv[it].lo), amax4(xv[it].hi)));
+        const float m = fmaxf(amax4(xv[it].lo), amax4(xv[it].hi));
+        amax = fmaxf(amax, (it * WGW + wid) * 4 + r4 < NBLK ? m : 0.0f);
     }
     amax = wave_max_f32(amax);
     if (lane == 0) red[wid] = amax;
@@ -179,10 +180,21 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_kernel(const floa
         s = sio[0];
     }
 
-    // 2. the first D weight loads (rows 0 .. R-1), kept behind the token's
-    //    loads and ahead of the rotation, which then waits for the token only
+    // 2. the scales of rows 0 .. R-1 (each row's NS scale dwords, lane l
+    //    holding dword l % NS, and its row scale), then the first D weight
+    //    loads (rows 0 .. R-1), all behind the token's loads and ahead of the
+    //    rotation, which then waits for the token only.  Issued after the
+    //    rotation, the scales cost the first row a whole memory latency.
+    auto sload = [&](int j) -> uint32_t { return gscale[static_cast<int64_t>(row_of(j)) * NS + lane % NS]; };
+    auto rload = [&](int j) -> uint32_t { return rscale[row_of(j)]; };
+    uint32_t scr[R], rsr[R];
     v4i ring[D];
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        scr[rr] = sload(rr);
+        rsr[rr] = rload(rr);
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i) ring[i] = wload(i / NS, i % NS);
     __builtin_amdgcn_sched_barrier(0);
@@ -194,19 +206,10 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_kernel(const floa
         for (int t = 0; t < NS; ++t) a[t] = *reinterpret_cast<const v4i *>(&q_lds[1024 * t + 16 * lane]);
     }
 
-    // 4. the weight stream, R rows per turn of the ring.  Each row's NS scale
-    //    dwords (lane l holds dword l % NS) and its row scale ride in the ring
-    //    with the row's weight loads, issued R rows ahead and unconditionally,
-    //    so the compiler's in-order wait counts cover them.
+    // 4. the weight stream, R rows per turn of the ring.  A row's scales ride
+    //    in the ring with its weight loads, issued R rows ahead and
+    //    unconditionally, so the compiler's in-order wait counts cover them.
     const int shift = 8 * r4;                      // byte of a scale dword this lane takes
-    auto sload = [&](int j) -> uint32_t { return gscale[static_cast<int64_t>(row_of(j)) * NS + lane % NS]; };
-    auto rload = [&](int j) -> uint32_t { return rscale[row_of(j)]; };
-    uint32_t scr[R], rsr[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-        scr[rr] = sload(rr);
-        rsr[rr] = rload(rr);
-    }
     for (int gi = 0; gi < groups; ++gi) {
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
@@ -288,8 +291,15 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_head_kernel(const
         s = sio[0];
     }
 
+    // the first rows' scales, then the first ring, ahead of the rotation
+    auto sload = [&](int j) -> uint32_t {
+        return gscale[static_cast<int64_t>(row_of(j)) * SD + min(lane, SD - 1)];
+    };
+    uint32_t scr[R];
     v4i ring[D];
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) scr[rr] = sload(rr);
 #pragma unroll
     for (int i = 0; i < D; ++i) ring[i] = wload(i / NS, i % NS);
     __builtin_amdgcn_sched_barrier(0);
@@ -302,12 +312,6 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_head_kernel(const
 
     const int sperm = 4 * (lane / 16);             // byte address of this lane's scale lane at t = 0
     const int shift = 16 * ((lane >> 3) & 1);
-    auto sload = [&](int j) -> uint32_t {
-        return gscale[static_cast<int64_t>(row_of(j)) * SD + min(lane, SD - 1)];
-    };
-    uint32_t scr[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) scr[rr] = sload(rr);
     const float sy = s * 0x1p-7f;
     for (int gi = 0; gi < groups; ++gi) {
 #pragma unroll
@@ -401,8 +405,15 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_tbl4_kernel(const
         s = sio[0];
     }
 
+    // the first pairs' scales, then the first ring, ahead of the rotation
+    auto sload = [&](int j) -> uint32_t {
+        return gscale[static_cast<int64_t>(row_of(j)) * SD + min(l32, SD - 1)];
+    };
+    uint32_t scr[R];
     v4i ring[D];
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) scr[rr] = sload(rr);
 #pragma unroll
     for (int i = 0; i < D; ++i) ring[i] = wload(i / NS, i % NS);
     __builtin_amdgcn_sched_barrier(0);
@@ -419,12 +430,6 @@ __global__ __launch_bounds__(64 * kRowWgWaves) void decode_row_tbl4_kernel(const
     const Tbl4Masks tk = tbl4_masks();
     const int sperm = 4 * (32 * h + l32 / 8);      // byte address of this lane's scale lane at t = 0
     const int shift = 16 * ((l32 >> 2) & 1);
-    auto sload = [&](int j) -> uint32_t {
-        return gscale[static_cast<int64_t>(row_of(j)) * SD + min(l32, SD - 1)];
-    };
-    uint32_t scr[R];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) scr[rr] = sload(rr);
     const float sy = s * 0x1p-7f;
     for (int gi = 0; gi < groups; ++gi) {
 #pragma unroll

@@ -190,23 +190,40 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
             g = 2 * sp + half;
             amax = g < G ? bamax[g] : 0.0f;
         }
+        // candidate c's scale (and its reciprocal) is computed once per span
+        // by lane c of the group (lanes 0..15; a head span's second group:
+        // lanes 32..47, whose amax is that group's) and fetched by every lane
+        // of the group in the loop below: the same IEEE operations as
+        // evaluating it in every lane, without the per-candidate divisions
+        const int cl = lane & 15;
+        float d_l;
+        uint32_t st_l;
+        {
+            const float target = (amax * (static_cast<float>(64 - cl) / 64.0f)) / 127.0f;
+            if constexpr (FMT == kFmtU8) {
+                float u = 1.0f;
+                if (rv != 0.0f) u = fminf(fmaxf(__builtin_rintf(target / rv), 1.0f), 255.0f);
+                st_l = static_cast<uint32_t>(u);
+                d_l = rv * u;
+            } else {
+                st_l = bf16_rne(target);
+                d_l = bf16_to_f32(static_cast<uint16_t>(st_l));
+            }
+        }
+        [[maybe_unused]] const float rd_l = 1.0f / d_l;
+        auto fetch = [&](uint32_t v, int c) -> uint32_t {
+            if constexpr (FMT == kFmtU8)
+                return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), c));
+            else
+                return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * (32 * half + c), static_cast<int>(v)));
+        };
         float best_d = 0.0f;
         uint32_t best_stored = 0;
         double best_err = 0.0;
 #pragma unroll 1
         for (int c = 0; c < kWqCandidates; ++c) {
-            const float target = (amax * (static_cast<float>(64 - c) / 64.0f)) / 127.0f;
-            float d;
-            uint32_t stored;
-            if constexpr (FMT == kFmtU8) {
-                float u = 1.0f;
-                if (rv != 0.0f) u = fminf(fmaxf(__builtin_rintf(target / rv), 1.0f), 255.0f);
-                stored = static_cast<uint32_t>(u);
-                d = rv * u;
-            } else {
-                stored = bf16_rne(target);
-                d = bf16_to_f32(static_cast<uint16_t>(stored));
-            }
+            const float d = __uint_as_float(fetch(__float_as_uint(d_l), c));
+            const uint32_t stored = fetch(st_l, c);
             if constexpr (FMT == kFmtTbl4) {
                 float v0, v1, v2, v3;
                 tbl4_nearest(w.x, d, v0);
@@ -227,7 +244,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const float *__restri
             // else (any lane of the wave near a half-integer, or d outside
             // the normal range) through the division for the whole wave
             bool near = !(d >= 0x1p-120f && d <= 0x1p120f);
-            const float rd = 1.0f / d;
+            const float rd = __uint_as_float(fetch(__float_as_uint(rd_l), c));
             float q0 = wq_code_rcp(w.x, rd, near);
             float q1 = wq_code_rcp(w.y, rd, near);
             float q2 = wq_code_rcp(w.z, rd, near);

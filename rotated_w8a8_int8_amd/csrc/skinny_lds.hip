@@ -50,7 +50,7 @@ constexpr int kSlKC = 256;                         // K bytes per stage
 // issues the same number of 1 KiB direct loads per stage (the explicit waits
 // count them): where a stage's blocks do not split evenly over the waves, the
 // remainder loads a valid block again into a spare LDS area nobody reads.
-// Two-stage rings wait for every load and skip those re-loads.
+// Two-stage rings skip those re-loads (their waits count weight loads only).
 template <int MB_, int NW_, int NST_, bool NT_, bool NTY_> struct SlShape {
     static constexpr int MB = MB_, NW = NW_, NST = NST_;
     static constexpr bool NT = NT_;                                // weight loads nontemporal
@@ -86,6 +86,9 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     const void *__restrict__ gscale, const uint16_t *__restrict__ rscale, float *__restrict__ y,
     int32_t *__restrict__ partials, int M, int N, int K) {
     constexpr int MB = S::MB, NST = S::NST, DA = S::DA, DB = S::DB;
+    // each wave loads exactly its own 16 weight rows (4 blocks of 4 rows), the
+    // rows it alone reads: the schedule below refills them without a barrier
+    static_assert(DB == 4 && S::NB == 4 * S::NW, "a wave's weight blocks must be its own rows");
     constexpr int GPS = (FMT == kFmtU8) ? 1 : 2;      // groups per stage
     constexpr int KPG = 4 / GPS;                       // k-steps per group
     constexpr int ESZ = (FMT == kFmtU8) ? 1 : 2;       // bytes per group scale
@@ -135,15 +138,16 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     auto sc_dword = [&](int s) -> int64_t { return min(sc_byte(s) & ~static_cast<int64_t>(3), sc_last); };
 
     // stages past the end re-load the last one into a buffer nobody reads
-    // again, so every wait count below is uniform.  With two stages each wait
-    // is for all of a wave's loads, so the spare re-loads that even out the
-    // waves' counts are skipped (1.2% on both the 128-token trunk and the
-    // 64-token head shapes once the LDS reads were conflict-free).
-    auto issue_stage = [&](int s) {
+    // again, so every wait count below is uniform.  With two stages the wait
+    // counts only the weight loads issued after a stage's token blocks, so
+    // the spare token re-loads that even out the waves' counts are skipped
+    // (1.2% on both the 128-token trunk and the 64-token head shapes once the
+    // LDS reads were conflict-free).
+    // block numbers are wave-major, so the padding blocks of each operand
+    // form one range: A's first, then B's, in the spare area
+    auto issue_a = [&](int s) {
         const int sc = min(s, NS - 1);
         const int buf = s % NST;
-        // block numbers are wave-major, so the padding blocks of each operand
-        // form one range: A's first, then B's, in the spare area
 #pragma unroll
         for (int i = 0; i < DA; ++i) {
             const int blk = wu * DA + i;
@@ -152,6 +156,11 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
                                              : lds_offset(&Xs[0]) + 1024u * (blk - S::NA);
             dma16(q + static_cast<int64_t>(sc) * kSlKC, aoffs[i], dst);
         }
+    };
+    // a wave's weight blocks are its own 16 rows, and its scale dword theirs
+    auto issue_b = [&](int s) {
+        const int sc = min(s, NS - 1);
+        const int buf = s % NST;
 #pragma unroll
         for (int i = 0; i < DB; ++i) {
             const int blk = wu * DB + i;
@@ -180,16 +189,23 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_kernel(
     const int boff = sl_addr(16 * wid + j, qd);
 
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue_stage(p);
+    for (int p = 0; p < NST - 1; ++p) {
+        issue_b(p);
+        issue_a(p);
+    }
     for (int s = 0; s < NS; ++s) {
-        // stage s has landed once at most the loads of the NST - 2 stages
-        // issued after it remain
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * S::DMA) : "memory");
-        // every wave's loads of stage s are in LDS, and every wave is done
-        // with stage s - 1, whose buffer the next issue overwrites
+        // this wave is done with its weight rows of stage s - 1 (no other
+        // wave reads them), so their buffer takes stage s + NST - 1 at once,
+        // ahead of the wait and the barrier.  Stage s has landed once at most
+        // the loads issued after its token blocks remain: NST - 2 whole stages
+        // and these weight rows.  The barrier publishes every wave's token
+        // blocks of stage s and retires stage s - 1's, whose buffer the token
+        // blocks of stage s + NST - 1 then take.
+        issue_b(s + NST - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * S::DMA + DB + 1) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_stage(s + NST - 1);
+        issue_a(s + NST - 1);
         const int buf = s % NST;
         const int8_t *Ab = As[buf];
         const int8_t *Bb = Bs[buf];
@@ -269,6 +285,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
     constexpr int DA = (NA + NW - 1) / NW, DB = (NB + NW - 1) / NW;
     constexpr int SPARE = DA * NW - NA + DB * NW - NB;
     constexpr int DMA = DA + DB + 2;                   // + two scale dwords
+    static_assert(DB == 4 && NB == 4 * NW, "a wave's weight blocks must be its own rows");
     __shared__ __attribute__((aligned(1024))) int8_t As[NST][ABYTES];
     __shared__ __attribute__((aligned(1024))) int8_t Bs[NST][BBYTES];
     __shared__ __attribute__((aligned(1024))) int8_t Xs[SPARE > 0 ? SPARE * 1024 : 16];
@@ -305,7 +322,7 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
     // (a row's scales are 2 G bytes, G a multiple of 4)
     const uint32_t sc_row = static_cast<uint32_t>(min(nrow, N - 1)) * static_cast<uint32_t>(2 * G);
 
-    auto issue_stage = [&](int s) {
+    auto issue_a = [&](int s) {
         const int sc = min(s, NS - 1);
         const int buf = s % NST;
 #pragma unroll
@@ -315,6 +332,11 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
                                           : lds_offset(&Xs[0]) + 1024u * (blk - NA);
             dma16(q + static_cast<int64_t>(sc) * RA, aoffs[i], dst);
         }
+    };
+    // a wave's weight blocks are its own 16 rows, and its scale dwords theirs
+    auto issue_b = [&](int s) {
+        const int sc = min(s, NS - 1);
+        const int buf = s % NST;
 #pragma unroll
         for (int i = 0; i < DB; ++i) {
             const int blk = wu * DB + i;
@@ -345,12 +367,18 @@ __global__ __launch_bounds__(64 * S::NW) void skinny_lds_tbl4_kernel(
 
     const Tbl4Masks tk = tbl4_masks();
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p) issue_stage(p);
+    for (int p = 0; p < NST - 1; ++p) {
+        issue_b(p);
+        issue_a(p);
+    }
     for (int s = 0; s < NS; ++s) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * DMA) : "memory");
+        // as in the kernel above: this wave's own weight rows first, then the
+        // wait, the barrier and the token blocks
+        issue_b(s + NST - 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * DMA + DB + 2) : "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue_stage(s + NST - 1);
+        issue_a(s + NST - 1);
         const int buf = s % NST;
         const int8_t *Ab = As[buf];
         const int8_t *Bb = Bs[buf];

@@ -14,8 +14,11 @@ single fused kernel; otherwise the quantiser followed by the GEMV path for
 M <= 128 or the GEMM path above).  The default workload is the single-token
 decode of the fused gate_up projection (M=1, K=5120, N=34816); the same run
 then measures the metric's other half, the 8K-token prefill through the down
-projection (M=8192, K=17408, N=5120), and reports it under "prefill_down"
-(--only skips it).
+projection (M=8192, K=17408, N=5120), and reports it under "prefill_down", and
+the metric's other two M <= 128 configurations, the speculative-verify batch
+(M=128, K=5120, N=34816) and the vocabulary head (M=64, K=5120, N=152064),
+under "verify_skinny" and "vocab_head", their oracle baselines on a shorter
+sample (--only skips all three).
 
 Each workload runs `--warmup` untimed steps (the first one eager, before any
 graph capture), then exactly `--steps` timed steps between two HIP events on
@@ -78,6 +81,8 @@ METRIC = "W8A8 rotated linear: HBM GB/s (M≤128) and int8 TOPS (M=8192), % of r
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 COPY_TARGET_BYTES = 1 << 30    # distinct weight bytes rotated through per round
+EXTRA_WORKLOADS = ("verify_skinny", "vocab_head")   # also timed by the default run
+EXTRA_CPU_SECONDS = 4.0        # oracle sample per extra workload
 PEAK_CLOCK_MHZ = 2400.0        # MI355X peak engine clock, at which the published peaks hold
 DEFAULT_WORKLOAD = "decode_gate_up"
 DEFAULT_STEPS = 200            # timed steps when --steps is not given
@@ -400,6 +405,16 @@ def main():
         out["prefill_down"] = {k: pre[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step",
                                                    "config", "roofline", "cpu_baseline",
                                                    "parity_on_timed_buffers")}
+        # the metric's other M <= 128 configurations: the speculative-verify
+        # batch and the vocabulary head, same step and warm-up counts, the
+        # oracle on a shorter sample
+        short = argparse.Namespace(**vars(args))
+        short.cpu_seconds = min(args.cpu_seconds, EXTRA_CPU_SECONDS)
+        for name in EXTRA_WORKLOADS:
+            rec = bench_linear(short, W.WORKLOADS[name])
+            out[name] = {k: rec[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step",
+                                             "config", "roofline", "cpu_baseline",
+                                             "parity_on_timed_buffers")}
     print(json.dumps(out))
 
 

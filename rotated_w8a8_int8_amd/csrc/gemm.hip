@@ -301,10 +301,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
             for (int kk = 0; kk < kSteps; ++kk) {
                 const int pos = st * kSteps + kk;      // k-step within the group
                 if (kk + 1 < kSteps) read_frags(kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+                // serpentine tile order, (0,0) (0,1) (1,1) (1,0): consecutive
+                // matrix ops share one operand, so fewer operand bits toggle;
+                // at the power limit the energy per op sets the time
 #pragma unroll
                 for (int tm = 0; tm < kTM; ++tm)
 #pragma unroll
-                    for (int tn = 0; tn < kTN; ++tn) {
+                    for (int tn_ = 0; tn_ < kTN; ++tn_) {
+                        const int tn = (tm & 1) ? kTN - 1 - tn_ : tn_;
                         const v4i a = fa[kk & 1][tm], b = fb[kk & 1][tn];
                         P[H][tm][tn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                             a, b, pos == 0 ? v16i{} : P[H][tm][tn], 0, 0, 0);

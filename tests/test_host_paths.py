@@ -101,3 +101,16 @@ def test_one_token_kernel_sources_follow_the_launch_rules():
     assert bench.kernel_sources(W.Workload("x", 1, 17408, 10, W.FMT_BF16G128, ""))[0] == "gemv.hip"
     assert bench.kernel_sources(W.Workload("x", 1, 10240, 10, W.FMT_TBL4_BF16G128, ""))[0] == "gemv.hip"
     assert bench.kernel_sources(W.WORKLOADS["prefill_down"])[0] == "gemm.hip"
+
+
+def test_bench_default_run_covers_every_configuration_of_the_metric():
+    # the default run times the decode step and, in the same JSON line, the
+    # prefill GEMM and the two other configurations with at most 128 tokens
+    sys.path.insert(0, ROOT)
+    import bench
+    from rotated_w8a8_int8_amd import workloads as W
+    assert bench.DEFAULT_WORKLOAD == "decode_gate_up"
+    shapes = {(W.WORKLOADS[n].M, W.WORKLOADS[n].K, W.WORKLOADS[n].N) for n in bench.EXTRA_WORKLOADS}
+    assert shapes == {(128, 5120, 34816), (64, 5120, 152064)}
+    assert all(W.WORKLOADS[n].M <= 128 for n in bench.EXTRA_WORKLOADS)
+    assert 0 < bench.EXTRA_CPU_SECONDS <= 12

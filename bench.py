@@ -6,6 +6,7 @@
     python bench.py --op kv_quant | kv_dequant [--workload kv_200k]
     python bench.py --op rescore [--workload vocab_head]
     python bench.py --op fwht | quant_act [--workload prefill_down]
+    python bench.py --op mfma_ceiling
 
 A step is one pass of the whole layer over one batch of synthetic input that
 is already resident in HBM: rad_w8a8_linear, which rotates + quantises the f32
@@ -57,6 +58,15 @@ f32 (8 bytes per element), rad_quant_act_i8 with rotation reads f32 and writes
 int8 codes plus one f32 scale per token (5 bytes per element + 4 per token);
 both are HBM streams against the 8 TB/s peak, launched eagerly over enough
 copies of the activations to exceed the last-level cache.
+
+--op mfma_ceiling times the matrix-core probe (rad_probe_mfma_i8, a
+measurement aid) at the prefill's operation count: back-to-back int8 32x32x32
+matrix ops with operands held in registers, and with each k-step's fragments
+read from LDS first (the reads an LDS-staged GEMM of 64 x 64 wave tiles must
+make), each on random and on constant bytes, with the clock and power while
+they run.  The prefill record's roofline carries the LDS-fed random-byte rate
+as `ceiling` and the GEMM's rate over it as `frac_of_ceiling`: on random codes
+the chip's power limit holds the matrix cores below the published peak.
 
 --op rescore times rad_w8a8_rescore on the workload's weight (default the
 vocabulary head) with 32 distinct candidate rows per token: 64 different
@@ -111,12 +121,14 @@ def parse():
                          "codes of 127) or by zeros, to see how the codes' switching moves the "
                          "power and clock (the default is the workload's random codes)")
     ap.add_argument("--op", choices=("linear", "quant_weight", "kv_quant", "kv_dequant", "rescore",
-                                     "fwht", "quant_act"),
+                                     "fwht", "quant_act", "mfma_ceiling"),
                     default="linear",
                     help="linear: the whole layer (default); quant_weight: the weight-side "
                          "quantiser on the workload's weight shape; kv_quant / kv_dequant: "
                          "the int8 KV-cache codec (workload kv_200k or kv_tiny); rescore: "
-                         "32 candidate rows per token of the workload's weight")
+                         "32 candidate rows per token of the workload's weight; mfma_ceiling: "
+                         "the matrix-core probe (register-fed and LDS-fed) on random and constant "
+                         "bytes, at the prefill's operation count")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python, no graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--vendor", action="store_true",
@@ -394,6 +406,9 @@ def main():
     if args.op in ("fwht", "quant_act"):
         bench_act(args, W.WORKLOADS["prefill_down"] if args.workload == DEFAULT_WORKLOAD else wl)
         return
+    if args.op == "mfma_ceiling":
+        bench_mfma_ceiling(args)
+        return
     if args.op == "rescore":
         bench_rescore(args, W.WORKLOADS["vocab_head"] if args.workload == DEFAULT_WORKLOAD else wl)
         return
@@ -566,6 +581,14 @@ def bench_linear(args, wl):
             roof["clock"] = clk
             roof["peak_at_clock"] = round(INT8_PEAK_TOPS * clk["gfx_clock_mhz"] / PEAK_CLOCK_MHZ, 1)
             roof["frac_at_clock"] = round(achieved / roof["peak_at_clock"], 4)
+        # what the matrix cores reach on random codes at all: the probe's
+        # LDS-fed mode (each k-step's fragments read from LDS, as this
+        # kernel's 64 x 64 wave tiles need; no memory traffic, no group fold)
+        # at the same operation count, timed right after
+        ceil = probe_rate(sz["ops"], lds_fed=True, random=True, steps=20, warmup=10,
+                          clock=not args.no_clock)
+        roof["ceiling"] = ceil
+        roof["frac_of_ceiling"] = round(achieved / ceil["tops"], 4)
 
 
     # ---- context: the vendor's int8 GEMM on the same codes (same stream,
@@ -945,6 +968,66 @@ def bench_act(args, wl):
         "cpu_baseline": cpu,
         "parity_on_timed_buffers": parity,
     }))
+
+
+def probe_rate(ops, lds_fed, random, steps, warmup, clock=True):
+    """int8 TOPS of the matrix-core probe (rad_probe_mfma_i8, one block per
+    CU) at about `ops` operations a launch, on random or constant bytes, with
+    the clock and power read while it runs back to back."""
+    import torch
+    from rotated_w8a8_int8_amd import binding as B
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    per_kstep = blocks * 8 * 4 * 65536
+    ksteps = max(2, 2 * int(round(ops / per_kstep / 2)))
+    n = blocks * B.RAD_PROBE_BLOCK_BYTES
+    if random:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        src = torch.randint(-127, 128, (n,), dtype=torch.int8, device="cuda", generator=g)
+    else:
+        src = torch.full((n,), 37, dtype=torch.int8, device="cuda")
+    out = torch.empty((blocks * 512,), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()                       # default priority
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            B.probe_mfma_i8(src, blocks, ksteps, lds_fed, out=out)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            B.probe_mfma_i8(src, blocks, ksteps, lds_fed, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    done = per_kstep * ksteps
+    rec = {"mode": "lds_fed" if lds_fed else "register_fed", "data": "random" if random else "constant",
+           "ops_per_launch": done, "us_per_launch": round(us, 1), "tops": round(done / (us * 1e-6) / 1e12, 1),
+           "frac": round(done / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4), "blocks": blocks, "ksteps": ksteps}
+    if clock:
+        def again():
+            with torch.cuda.stream(stream):
+                for _ in range(20):
+                    B.probe_mfma_i8(src, blocks, ksteps, lds_fed, out=out)
+        clk = sustained_clock(again, seconds=1.5)
+        if clk is not None:
+            rec["gfx_clock_mhz"] = clk["gfx_clock_mhz"]
+            rec["socket_power_w"] = clk["socket_power_w"]
+    return rec
+
+
+def bench_mfma_ceiling(args):
+    """The matrix-core probe at the prefill's operation count: register-fed
+    and LDS-fed, on random and on constant bytes."""
+    from rotated_w8a8_int8_amd import workloads as W
+    wl = W.WORKLOADS["prefill_down"]
+    ops = sizes(wl)["ops"]
+    steps = args.steps if args.steps is not None else 50
+    warmup = args.warmup if args.warmup is not None else 20
+    recs = [probe_rate(ops, lds_fed, random, steps, warmup, clock=not args.no_clock)
+            for lds_fed in (False, True) for random in (True, False)]
+    print(json.dumps({"metric": "int8 matrix-core probe, TOPS at the prefill_down operation count",
+                      "unit": "TOPS", "peak": INT8_PEAK_TOPS, "steps": steps, "warmup": warmup,
+                      "records": recs}))
 
 
 def bench_kv(args):

@@ -291,6 +291,39 @@ int rad_kv_quant_i8(const uint16_t *x, int8_t *codes, uint16_t *scale, int64_t r
 int rad_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, int64_t rows,
                       int64_t D, rad_stream_t stream);
 
+/*
+ * rad_probe_mfma_i8 -- a measurement aid, not a step of the layer: what the
+ * int8 matrix cores sustain on given operand bytes.  Its callers are
+ * benchmarks that price a contraction against the rate the chip reaches on
+ * the same kind of data within its power budget (on random codes the core
+ * clock stays well below its maximum).
+ *
+ * Launches `blocks` workgroups of 8 waves (one per CU at most: each takes
+ * 96 KiB of LDS).  Block b copies its RAD_PROBE_BLOCK_BYTES of `src` (bytes
+ * b * RAD_PROBE_BLOCK_BYTES ..) into LDS; each wave then runs `ksteps`
+ * k-steps of a 64 x 64 tile, four v_mfma_i32_32x32x32_i8 a k-step (32 x 32
+ * outputs over 32 of K each), on 16-byte fragments of those bytes.
+ * lds_fed = 0: the fragments are loaded once and the wave alternates between
+ * two sets; lds_fed = 1: every k-step's four fragments are read from LDS
+ * first, as an LDS-staged GEMM with this wave tile must.  The int8 operations
+ * performed are blocks * 8 * ksteps * 4 * 65536.
+ *
+ *   src     int8 [blocks * RAD_PROBE_BLOCK_BYTES], 16-byte aligned.
+ *   out     int32 [blocks * 512]: each lane's 64 accumulator elements summed
+ *           with 32-bit wrap-around.  With every src byte equal to c each
+ *           word is 2048 * ksteps * c * c (mod 2^32).
+ *   blocks  0 .. RAD_PROBE_MAX_BLOCKS; ksteps even, 0 .. RAD_PROBE_MAX_KSTEPS.
+ *
+ * Errors: RAD_E_SHAPE (negative or odd ksteps, negative blocks), RAD_E_RANGE
+ * (sizes above the maxima, lds_fed not 0 or 1), RAD_E_NULL, RAD_E_ALIGN,
+ * RAD_E_ALIAS (out overlaps src).
+ */
+#define RAD_PROBE_BLOCK_BYTES 98304
+#define RAD_PROBE_MAX_BLOCKS 65536
+#define RAD_PROBE_MAX_KSTEPS 1073741824
+int rad_probe_mfma_i8(const int8_t *src, int32_t *out, int64_t blocks, int64_t ksteps, int lds_fed,
+                      rad_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *rad_strerror(int status);
 

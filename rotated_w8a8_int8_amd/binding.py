@@ -33,10 +33,13 @@ RAD_QUANT_MAX_K = 65536
 RAD_GEMV_MAX_M = 128
 RAD_QUANT_WEIGHT_MAX_K = 32768
 RAD_LINEAR_MAX_K = 16777216
+RAD_PROBE_BLOCK_BYTES = 98304
+RAD_PROBE_MAX_BLOCKS = 65536
+RAD_PROBE_MAX_KSTEPS = 1073741824
 
 EXPORTS = ("rad_fwht128", "rad_quant_act_i8", "rad_w8a8_gemv", "rad_w8a8_gemm", "rad_w8a8_linear",
            "rad_quant_weight_i8", "rad_kv_quant_i8", "rad_kv_dequant_i8", "rad_w8a8_rescore",
-           "rad_strerror")
+           "rad_probe_mfma_i8", "rad_strerror")
 KV_HEAD_DIMS = (64, 128, 256)
 
 
@@ -78,9 +81,10 @@ def lib() -> ctypes.CDLL:
         L.rad_kv_quant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
         L.rad_kv_dequant_i8.argtypes = [vp, vp, vp, i64, i64, vp]
         L.rad_w8a8_rescore.argtypes = [vp, vp, ctypes.POINTER(WeightDesc), vp, i64, vp, i64, vp]
+        L.rad_probe_mfma_i8.argtypes = [vp, vp, i64, i64, ci, vp]
         for f in (L.rad_fwht128, L.rad_quant_act_i8, L.rad_w8a8_gemv, L.rad_w8a8_gemm,
                   L.rad_w8a8_linear, L.rad_quant_weight_i8, L.rad_kv_quant_i8, L.rad_kv_dequant_i8,
-                  L.rad_w8a8_rescore):
+                  L.rad_w8a8_rescore, L.rad_probe_mfma_i8):
             f.restype = ci
         L.rad_strerror.argtypes = [ci]
         L.rad_strerror.restype = ctypes.c_char_p
@@ -369,3 +373,23 @@ def w8a8_rescore(q, scale, w: W8A8Weight, ids, y=None):
     _check(lib().rad_w8a8_rescore(q.data_ptr(), scale.data_ptr(), ctypes.byref(d), ids.data_ptr(), C,
                                   y.data_ptr(), M, _stream(q)), "rad_w8a8_rescore")
     return y
+
+
+def probe_mfma_i8(src, blocks: int, ksteps: int, lds_fed: bool, out=None):
+    """Measurement aid (not a step of the layer): ``ksteps`` k-steps of four
+    int8 32x32x32 matrix ops per wave, 8 waves per block, on the operand bytes
+    ``src`` (int8, ``blocks * RAD_PROBE_BLOCK_BYTES``); returns the int32
+    [blocks * 512] per-lane accumulator sums.  Performs
+    ``blocks * 8 * ksteps * 4 * 65536`` int8 operations."""
+    torch = _torch()
+    _dev(src, torch.int8, "src")
+    if src.numel() != blocks * RAD_PROBE_BLOCK_BYTES:
+        raise ValueError("src has %d bytes, expected %d" % (src.numel(), blocks * RAD_PROBE_BLOCK_BYTES))
+    if out is None:
+        out = torch.empty((blocks * 512,), dtype=torch.int32, device=src.device)
+    _dev(out, torch.int32, "out")
+    _shape(out, (blocks * 512,), "out")
+    _same_device(src, (out, "out"))
+    _check(lib().rad_probe_mfma_i8(src.data_ptr(), out.data_ptr(), blocks, ksteps, 1 if lds_fed else 0,
+                                   _stream(src)), "rad_probe_mfma_i8")
+    return out

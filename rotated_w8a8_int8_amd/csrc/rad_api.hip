@@ -42,6 +42,7 @@ int64_t checked_mul(std::initializer_list<int64_t> xs) {
     return r;
 }
 static_assert(RAD_QUANT_WEIGHT_MAX_K == rad::kQuantWeightMaxK, "header and kernel agree on the largest K");
+static_assert(RAD_PROBE_BLOCK_BYTES == rad::kProbeBlockBytes, "header and kernel agree on a probe block");
 
 int group_width(int32_t fmt) {
     if (fmt == RAD_FMT_U8G256_BF16ROW) return 256;
@@ -248,6 +249,19 @@ int rad_kv_dequant_i8(const int8_t *codes, const uint16_t *scale, uint16_t *y, i
     const int rc = check_kv(y, codes, scale, rows, D);
     if (rc != RAD_OK) return rc > 0 ? RAD_OK : rc;
     return hip_status(rad::launch_kv_dequant(codes, scale, y, rows, D, static_cast<hipStream_t>(stream)));
+}
+
+int rad_probe_mfma_i8(const int8_t *src, int32_t *out, int64_t blocks, int64_t ksteps, int lds_fed,
+                      rad_stream_t stream) {
+    if (blocks < 0 || ksteps < 0 || ksteps % 2 != 0) return RAD_E_SHAPE;
+    if (blocks > RAD_PROBE_MAX_BLOCKS || ksteps > RAD_PROBE_MAX_KSTEPS || (lds_fed != 0 && lds_fed != 1))
+        return RAD_E_RANGE;
+    if (blocks == 0 || ksteps == 0) return RAD_OK;
+    if (!src || !out) return RAD_E_NULL;
+    if (!aligned(src, 16) || !aligned(out, 4)) return RAD_E_ALIGN;
+    if (overlap(span(src, blocks * rad::kProbeBlockBytes), span(out, blocks * 512 * 4))) return RAD_E_ALIAS;
+    return hip_status(rad::launch_mfma_probe(src, out, blocks, ksteps, lds_fed == 1,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 const char *rad_strerror(int status) {

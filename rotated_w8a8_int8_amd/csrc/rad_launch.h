@@ -57,5 +57,11 @@ hipError_t launch_gemm(const int8_t *q, const float *s, const WeightArgs &w, flo
                        int32_t *partials, hipStream_t st);
 // Whether launch_gemm's grid (one workgroup per output tile) fits a launch.
 bool gemm_grid_fits(int64_t M, int64_t N);
+// Measurement aid: back-to-back int8 matrix ops, one 8-wave workgroup per
+// block, each block reading its own kProbeBlockBytes of operand bytes; every
+// lane writes one 32-bit word (blocks * 512 words in all).
+constexpr int kProbeBlockBytes = 96 * 1024;
+hipError_t launch_mfma_probe(const int8_t *src, int32_t *out, int64_t blocks, int64_t ksteps, bool lds_fed,
+                             hipStream_t st);
 
 }  // namespace rad

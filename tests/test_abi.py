@@ -253,3 +253,31 @@ def test_codebook_format_validation():
     q = B.lib().rad_quant_weight_i8
     assert q(A, Bp, C, D, 4, 512, TBL, None) == B.RAD_E_FMT                               # no row scales
     assert q(A, Bp, Bp + 4 * 256 - 64, None, 4, 512, TBL, None) == B.RAD_E_ALIAS          # scales in codes
+
+
+# ---------------------------------------------------- matrix-core probe --
+
+def test_probe_validation():
+    L = B.lib()
+    P = L.rad_probe_mfma_i8
+    assert P(A, Bp, 1, -2, 0, None) == B.RAD_E_SHAPE            # negative k-steps
+    assert P(A, Bp, 1, 3, 0, None) == B.RAD_E_SHAPE             # odd k-steps
+    assert P(A, Bp, -1, 2, 0, None) == B.RAD_E_SHAPE
+    assert P(A, Bp, B.RAD_PROBE_MAX_BLOCKS + 1, 2, 0, None) == B.RAD_E_RANGE
+    assert P(A, Bp, 1, B.RAD_PROBE_MAX_KSTEPS + 2, 0, None) == B.RAD_E_RANGE
+    assert P(A, Bp, 1, 2, 2, None) == B.RAD_E_RANGE             # mode is 0 or 1
+    assert P(NULLS, NULLS, 0, 2, 1, None) == B.RAD_OK           # empty: nothing launched
+    assert P(NULLS, NULLS, 4, 0, 1, None) == B.RAD_OK
+    assert P(NULLS, Bp, 1, 2, 0, None) == B.RAD_E_NULL
+    assert P(A, NULLS, 1, 2, 0, None) == B.RAD_E_NULL
+    assert P(A + 8, Bp, 1, 2, 0, None) == B.RAD_E_ALIGN
+    assert P(A, Bp + 2, 1, 2, 0, None) == B.RAD_E_ALIGN
+    # out inside the 2 blocks x 96 KiB of src
+    assert P(A, A + B.RAD_PROBE_BLOCK_BYTES, 2, 2, 1, None) == B.RAD_E_ALIAS
+
+
+def test_probe_constants_match_header():
+    h = header_text()
+    for name in ("RAD_PROBE_BLOCK_BYTES", "RAD_PROBE_MAX_BLOCKS", "RAD_PROBE_MAX_KSTEPS"):
+        m = re.search(r"#define %s (\d+)" % name, h)
+        assert m and int(m.group(1)) == getattr(B, name), name
